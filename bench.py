@@ -1,0 +1,255 @@
+"""Benchmark of the groupwise low-bit linear hot path on one MI355X.
+
+One step = one pass of the hot path over the headline workloads:
+  * decode (qmv): M=1, K=N=4096, group 64, fp16 activations, bits 1..7 --
+    the Llama-3.1-8B-shaped decode linears at K=N=4096;
+  * batched (qmm, MFMA): M=128, bits 4, group 128, bf16, (K, N) = (4096, 14336)
+    and (14336, 4096).
+Inputs are seeded synthetic tensors (no checkpoints), already resident in GPU
+memory when timing starts; weights are quantized and packed on the GPU before
+timing (quantization is one-off, not on the decode path).  To keep the
+256 MB Infinity Cache from serving repeated weights, every step reads a
+different copy of all weights from a rotating set of >= 1 GiB.
+
+Printed: one JSON line.  `value` is the decode kernels' achieved algorithmic
+HBM bandwidth over bits 1..7 (sum of bytes / sum of kernel times); per-bit
+microseconds and GB/s and the batched kernel's TFLOP/s are extra fields.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+ROTATE_BYTES = 1 << 30
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=50,
+                    help="launches per kernel in the per-kernel timing loops")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-reps", type=int, default=30)
+    return ap.parse_args()
+
+
+def qmv_cases():
+    from bit_groupwise_weight_amd.workloads import Case
+    return [Case(f"llama8b_k4096_n4096_b{b}_g64", 1, 4096, 4096, b, 64, "f16") for b in range(1, 8)]
+
+
+def qmm_cases():
+    from bit_groupwise_weight_amd.workloads import batched_qmm
+    return batched_qmm()
+
+
+def algo_bytes(case) -> int:
+    """Bytes the layer must move: packed codes + scales + zeros + x + y (+ bias)."""
+    e = {"f32": 4, "f16": 2, "bf16": 2}[case.act]
+    b = case.N * case.K * case.bits // 8 + 2 * case.N * (case.K // case.group) * e
+    b += case.M * case.K * e + case.M * case.N * e
+    if case.bias:
+        b += case.N * e
+    return b
+
+
+def prepare(case, copies, dev):
+    """Quantize once on the GPU and make `copies` independent copies of the weights."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    from bit_groupwise_weight_amd.workloads import make_bias, make_weight, make_x
+    act = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.act]
+    W = make_weight(case).to(dev)
+    packed, s, z, _ = lb.lowbit_quantize_pack(W, case.bits, case.group, act)
+    del W
+    x = make_x(case).to(dev)
+    b = make_bias(case)
+    b = None if b is None else b.to(dev)
+    sets = [(packed, s, z)] + [(packed.clone(), s.clone(), z.clone()) for _ in range(copies - 1)]
+    ys = [torch.empty((case.M, case.N), dtype=act, device=dev) for _ in range(2)]
+    return {"case": case, "sets": sets, "x": x, "bias": b, "ys": ys}
+
+
+def launch(p, i, stream):
+    from bit_groupwise_weight_amd import lowbit as lb
+    c = p["case"]
+    packed, s, z = p["sets"][i % len(p["sets"])]
+    lb.lowbit_linear(p["x"], packed, s, z, p["bias"], c.bits, c.group, y=p["ys"][i % 2],
+                     stream=stream)
+
+
+def time_kernel(p, reps, stream):
+    """Average time of one launch over `reps` back-to-back launches (rotating
+    weight copies), from HIP events recorded on the launch stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for i in range(3):
+        launch(p, i, stream)
+    e0.record(stream)
+    for i in range(reps):
+        launch(p, i, stream)
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps   # microseconds
+
+
+def cpu_baseline(cases, reps):
+    """The CPU oracle's linear (fp64 dequant + matmul) timed on this host."""
+    import oracle
+    from bit_groupwise_weight_amd.workloads import make_bias, make_weight, make_x
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    total_bytes, total_s = 0, 0.0
+    for c in cases:
+        W = make_weight(c).numpy()
+        ref = oracle.quantize(W, c.bits, c.group, c.act)
+        x = make_x(c).float().numpy()
+        b = make_bias(c)
+        b = None if b is None else b.float().numpy()
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.linear(x, ref["q"], ref["s"], ref["z"], c.group, b)
+            total_s += time.perf_counter() - t0
+            total_bytes += algo_bytes(c)
+    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle linear (fp64 dequant + matmul) on the 7 decode cases "
+                      f"K=N=4096 g64 bits 1..7, {reps} reps each, {total_s:.1f} s total; "
+                      f"quantization excluded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by output rows, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    from bit_groupwise_weight_amd import lowbit as lb
+    lb.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    qcases, mcases = qmv_cases(), qmm_cases()
+    qmv_bytes_all = sum(algo_bytes(c) for c in qcases)
+    qmm_bytes_all = sum(algo_bytes(c) for c in mcases)
+    copies_qmv = max(2, -(-ROTATE_BYTES // qmv_bytes_all))
+    copies_qmm = max(2, -(-ROTATE_BYTES // qmm_bytes_all))
+    log(f"preparing: qmv copies={copies_qmv}, qmm copies={copies_qmm}")
+    qp = [prepare(c, copies_qmv, dev) for c in qcases]
+    mp = [prepare(c, copies_qmm, dev) for c in mcases]
+    torch.cuda.synchronize()
+
+    def step(i):
+        for p in qp:
+            launch(p, i, stream)
+        for p in mp:
+            launch(p, i, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host wall {wall_ms:.1f} ms)")
+
+    # per-kernel average launch durations (HIP events on the launch stream)
+    qmv_us = [time_kernel(p, args.reps, stream) for p in qp]
+    qmm_us = [time_kernel(p, args.reps, stream) for p in mp]
+    per_bit = []
+    for c, us in zip(qcases, qmv_us):
+        gbps = algo_bytes(c) / (us * 1e-6) / 1e9
+        per_bit.append({"bits": c.bits, "us": round(us, 3), "bytes": algo_bytes(c),
+                        "GB_s": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        log(f"qmv b={c.bits}: {us:.3f} us  {gbps:.1f} GB/s")
+    qmv_total_us = sum(qmv_us)
+    qmv_gbps = qmv_bytes_all / (qmv_total_us * 1e-6) / 1e9
+    qmm = []
+    for c, us in zip(mcases, qmm_us):
+        fl = 2.0 * c.M * c.N * c.K
+        tf = fl / (us * 1e-6) / 1e12
+        qmm.append({"K": c.K, "N": c.N, "M": c.M, "us": round(us, 3), "TFLOP_s": round(tf, 2),
+                    "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        log(f"qmm K={c.K} N={c.N}: {us:.3f} us  {tf:.2f} TFLOP/s")
+    qmm_fl = sum(2.0 * c.M * c.N * c.K for c in mcases)
+    qmm_tf = qmm_fl / (sum(qmm_us) * 1e-6) / 1e12
+
+    out = {
+        "metric": "qmv us & achieved HBM GB/s (bits 1-7, K=N=4096); qmm TFLOPS at M=128",
+        "value": round(qmv_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,0.02) weights quantized on the GPU, N(0,1) activations)",
+        "config": {
+            "workload": "decode linears M=1 K=N=4096 group 64 fp16 bits 1..7 (qmv) + batched "
+                        "M=128 bits 4 group 128 bf16 (K,N)=(4096,14336),(14336,4096) (qmm)",
+            "rotating_weight_bytes": int(ROTATE_BYTES),
+        },
+        "roofline": {
+            "kernel": "qmv (bits 1..7 instances, aggregated)",
+            "bound": "hbm",
+            "achieved": round(qmv_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(qmv_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "qmv_by_bits": per_bit,
+        "qmv_total_us": round(qmv_total_us, 3),
+        "roofline_qmm": {
+            "kernel": "qmm (M=128, bits 4, group 128, bf16)",
+            "bound": "mfma",
+            "achieved": round(qmm_tf, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(qmm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "qmm": qmm,
+        "timing": "per-kernel us = HIP-event time of a loop of back-to-back launches on the "
+                  "launch stream / launches",
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline(qcases, args.cpu_sample_reps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,67 @@
+// Launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+// Activation (and scale/zero) element types.
+enum ActKind : int { ACT_F32 = 0, ACT_F16 = 1, ACT_BF16 = 2 };
+
+// ---------------------------------------------------------------- quantize --
+struct QuantParams {
+  const float* w;      // N x K fp32
+  void* scales;        // N x G, sz dtype
+  void* zeros;         // N x G, sz dtype
+  uint8_t* packed;     // N x K*bits/8
+  uint8_t* codes;      // N x K or nullptr
+  int* status;         // [0] non-finite weight seen, [1] non-finite stored scale/zero
+  int64_t N, K;
+  int bits, group, sz_act;
+};
+hipError_t launch_quant_pack(const QuantParams& p, hipStream_t stream);
+
+// --------------------------------------------------------------------- qmv --
+struct QmvParams {
+  const void* x;          // M x K act
+  const uint8_t* packed;  // N x row_bytes
+  const void* scales;     // N x groups act
+  const void* zeros;      // N x groups act
+  const void* bias;       // N act or nullptr
+  void* y;                // M x N act
+  int M, N, K;
+  int units;              // ceil(K / 128): 128-code units per row
+  int lpr_shift;          // log2(lanes cooperating on one row group), <= 6
+  int groups;             // K / group
+  int64_t row_bytes;      // K * bits / 8
+  int aligned16;          // row_bytes % 16 == 0 (every row starts 16-byte aligned)
+};
+struct QmvLaunch {
+  dim3 grid, block;
+  int mt;                 // activation rows per pass: 1 or 4
+};
+// One entry point per bit width (compiled as separate objects).
+hipError_t launch_qmv_b1(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b2(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b3(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b4(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b5(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b6(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b7(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+
+// --------------------------------------------------------------------- qmm --
+struct QmmParams {
+  const void* x;
+  const uint8_t* packed;
+  const void* scales;
+  const void* zeros;
+  const void* bias;
+  void* y;
+  int M, N, K;
+  int groups;
+  int64_t row_bytes;
+};
+hipError_t launch_qmm(const QmmParams& p, int bits, int group, int act, hipStream_t stream);
+
+}  // namespace lowbit

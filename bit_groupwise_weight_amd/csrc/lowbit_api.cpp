@@ -1,0 +1,274 @@
+// Host side of the C ABI declared in include/lowbit.h: argument validation,
+// schedule selection and kernel dispatch.  Validation never touches the HIP
+// runtime, so every argument error is reported identically with or without a
+// GPU present.
+#include "lowbit.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lowbit_status fail(lowbit_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lowbit_status fail(lowbit_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+lowbit_status hip_fail(hipError_t e, const char* what) {
+  return fail(LOWBIT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_bits(int bits) { return bits >= 1 && bits <= 7; }
+bool valid_group(int g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+bool valid_dtype(lowbit_dtype d) { return d == LOWBIT_F32 || d == LOWBIT_F16 || d == LOWBIT_BF16; }
+size_t dtype_bytes(lowbit_dtype d) { return d == LOWBIT_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shapes are limited so that every element index fits the kernels' 32-bit
+// row/column counters and 64-bit offsets.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+lowbit_status check_common(int bits, int group, int64_t N, int64_t K) {
+  if (!valid_bits(bits)) return fail(LOWBIT_ERR_INVALID_ARG, "bits=%d not in 1..7", bits);
+  if (!valid_group(group))
+    return fail(LOWBIT_ERR_INVALID_ARG, "group=%d not one of 32/64/128/256", group);
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+    return fail(LOWBIT_ERR_INVALID_ARG, "N=%lld K=%lld must be in 1..2^30", (long long)N,
+                (long long)K);
+  if (K % group != 0)
+    return fail(LOWBIT_ERR_INVALID_ARG, "K=%lld is not a multiple of group=%d", (long long)K,
+                group);
+  return LOWBIT_OK;
+}
+
+// One status word pair per device for lowbit_quantize_pack, allocated on first
+// use and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_status_mu;
+int* g_status[kMaxDevices] = {};
+
+lowbit_status device_status_word(int** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LOWBIT_ERR_HIP, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_status_mu);
+  if (g_status[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipMalloc(&p, 2 * sizeof(int));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(status)");
+    g_status[dev] = static_cast<int*>(p);
+  }
+  *out = g_status[dev];
+  return LOWBIT_OK;
+}
+
+int act_kind(lowbit_dtype d) {
+  switch (d) {
+    case LOWBIT_F32: return lowbit::ACT_F32;
+    case LOWBIT_F16: return lowbit::ACT_F16;
+    default: return lowbit::ACT_BF16;
+  }
+}
+
+typedef hipError_t (*QmvLauncher)(const lowbit::QmvParams&, const lowbit::QmvLaunch&, int, int,
+                                  hipStream_t);
+const QmvLauncher kQmv[8] = {nullptr,
+                             lowbit::launch_qmv_b1,
+                             lowbit::launch_qmv_b2,
+                             lowbit::launch_qmv_b3,
+                             lowbit::launch_qmv_b4,
+                             lowbit::launch_qmv_b5,
+                             lowbit::launch_qmv_b6,
+                             lowbit::launch_qmv_b7};
+
+constexpr int64_t kQmmMinM = 16;
+
+lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
+                      const void* zeros, const void* bias, void* y, int bits, int group,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  lowbit::QmvParams p{};
+  p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.K = static_cast<int>(K);
+  p.units = static_cast<int>((K + 127) / 128);
+  p.groups = static_cast<int>(K / group);
+  p.row_bytes = K * bits / 8;
+  p.aligned16 = (p.row_bytes % 16) == 0;
+  int shift = 0;
+  while ((1 << shift) < p.units && shift < 6) ++shift;
+  p.lpr_shift = shift;
+
+  lowbit::QmvLaunch l{};
+  l.mt = (M == 1) ? 1 : 4;
+  const int R = (l.mt == 1) ? 2 : 1;
+  // Prefer 256-thread blocks; shrink them when that leaves too few blocks to
+  // cover the chip.
+  int threads = 256;
+  auto blocks_for = [&](int t) {
+    const int64_t rows_per_block = static_cast<int64_t>(t >> shift) * R;
+    return (N + rows_per_block - 1) / rows_per_block;
+  };
+  while (threads > 64 && blocks_for(threads) < 1024 && (threads >> 1) >= (1 << shift)) threads >>= 1;
+  const int64_t bx = blocks_for(threads);
+  const int64_t by = (M + l.mt - 1) / l.mt;
+  if (bx > 0x7fffffff || by > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "problem too large");
+  l.grid = dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by));
+  l.block = dim3(threads);
+  hipError_t e = kQmv[bits](p, l, group, act_kind(act), stream);
+  if (e != hipSuccess) return hip_fail(e, "qmv launch");
+  return LOWBIT_OK;
+}
+
+lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
+                      const void* zeros, const void* bias, void* y, int bits, int group,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  lowbit::QmmParams p{};
+  p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.K = static_cast<int>(K);
+  p.groups = static_cast<int>(K / group);
+  p.row_bytes = K * bits / 8;
+  if ((M + 63) / 64 > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "M too large for qmm");
+  hipError_t e = lowbit::launch_qmm(p, bits, group, act_kind(act), stream);
+  if (e != hipSuccess) return hip_fail(e, "qmm launch");
+  return LOWBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lowbit_abi_version(void) { return LOWBIT_ABI_VERSION; }
+
+size_t lowbit_packed_bytes(int bits, int64_t N, int64_t K) {
+  if (!valid_bits(bits) || N <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) * bits / 8;
+}
+
+int64_t lowbit_num_groups(int64_t K, int group) {
+  if (!valid_group(group) || K <= 0 || K % group != 0) return 0;
+  return K / group;
+}
+
+const char* lowbit_status_string(lowbit_status s) {
+  switch (s) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_ERR_INVALID_ARG: return "invalid argument";
+    case LOWBIT_ERR_UNSUPPORTED: return "unsupported combination";
+    case LOWBIT_ERR_MISALIGNED: return "misaligned pointer";
+    case LOWBIT_ERR_NONFINITE: return "non-finite weight";
+    case LOWBIT_ERR_RANGE: return "scale or zero out of range for its dtype";
+    case LOWBIT_ERR_WORKSPACE: return "bad workspace";
+    case LOWBIT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* lowbit_last_error(void) { return g_last_error.c_str(); }
+
+lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t N, int64_t K,
+                                   lowbit_dtype sz_dtype, void* scales, void* zeros,
+                                   uint8_t* packed, uint8_t* codes, void* stream) {
+  g_last_error.clear();
+  lowbit_status st = check_common(bits, group, N, K);
+  if (st != LOWBIT_OK) return st;
+  if (!valid_dtype(sz_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "sz_dtype=%d", (int)sz_dtype);
+  if (!w || !scales || !zeros || !packed) return fail(LOWBIT_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(w, 16)) return fail(LOWBIT_ERR_MISALIGNED, "w must be 16-byte aligned");
+  if (!aligned(packed, 16)) return fail(LOWBIT_ERR_MISALIGNED, "packed must be 16-byte aligned");
+  const size_t e = dtype_bytes(sz_dtype);
+  if (!aligned(scales, e) || !aligned(zeros, e))
+    return fail(LOWBIT_ERR_MISALIGNED, "scales/zeros must be aligned to their element size");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* status = nullptr;
+  st = device_status_word(&status);
+  if (st != LOWBIT_OK) return st;
+  hipError_t he = hipMemsetAsync(status, 0, 2 * sizeof(int), s);
+  if (he != hipSuccess) return hip_fail(he, "hipMemsetAsync(status)");
+  lowbit::QuantParams p{};
+  p.w = w; p.scales = scales; p.zeros = zeros; p.packed = packed; p.codes = codes;
+  p.status = status; p.N = N; p.K = K; p.bits = bits; p.group = group;
+  p.sz_act = act_kind(sz_dtype);
+  he = lowbit::launch_quant_pack(p, s);
+  if (he != hipSuccess) return hip_fail(he, "quant_pack launch");
+  int host[2] = {0, 0};
+  he = hipMemcpyAsync(host, status, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(status)");
+  he = hipStreamSynchronize(s);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize");
+  if (host[0]) return fail(LOWBIT_ERR_NONFINITE, "weight holds a NaN or infinity");
+  if (host[1]) return fail(LOWBIT_ERR_RANGE, "a scale or zero is not finite in its dtype");
+  return LOWBIT_OK;
+}
+
+size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, int64_t K,
+                                     lowbit_dtype act_dtype) {
+  (void)bits; (void)group; (void)M; (void)N; (void)K; (void)act_dtype;
+  return 0;
+}
+
+lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                                 const void* scales, const void* zeros, const void* bias, void* y,
+                                 int bits, int group, int64_t M, int64_t N, int64_t K,
+                                 void* workspace, size_t workspace_bytes, lowbit_path path,
+                                 void* stream) {
+  g_last_error.clear();
+  lowbit_status st = check_common(bits, group, N, K);
+  if (st != LOWBIT_OK) return st;
+  if (M < 0 || M > kMaxDim) return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld", (long long)M);
+  if (!valid_dtype(act_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "act_dtype=%d", (int)act_dtype);
+  if (path != LOWBIT_PATH_AUTO && path != LOWBIT_PATH_QMV && path != LOWBIT_PATH_QMM)
+    return fail(LOWBIT_ERR_INVALID_ARG, "path=%d", (int)path);
+  if (workspace == nullptr && workspace_bytes != 0)
+    return fail(LOWBIT_ERR_WORKSPACE, "workspace_bytes > 0 with a NULL workspace");
+  if (workspace != nullptr && !aligned(workspace, 256))
+    return fail(LOWBIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (!packed || !scales || !zeros) return fail(LOWBIT_ERR_INVALID_ARG, "NULL weight pointer");
+  if (M > 0 && (!x || !y)) return fail(LOWBIT_ERR_INVALID_ARG, "NULL x or y");
+  if (!aligned(packed, 16)) return fail(LOWBIT_ERR_MISALIGNED, "packed must be 16-byte aligned");
+  if (!aligned(x, 16)) return fail(LOWBIT_ERR_MISALIGNED, "x must be 16-byte aligned");
+  const size_t e = dtype_bytes(act_dtype);
+  if (!aligned(scales, e) || !aligned(zeros, e) || !aligned(y, e) || (bias && !aligned(bias, e)))
+    return fail(LOWBIT_ERR_MISALIGNED, "scales/zeros/bias/y must be aligned to their element size");
+  if (path == LOWBIT_PATH_QMM && act_dtype == LOWBIT_F32)
+    return fail(LOWBIT_ERR_UNSUPPORTED, "the MFMA path takes fp16 or bf16 activations");
+  if (M == 0) return LOWBIT_OK;
+
+  bool use_qmm;
+  if (path == LOWBIT_PATH_QMV) use_qmm = false;
+  else if (path == LOWBIT_PATH_QMM) use_qmm = true;
+  else use_qmm = (M >= kQmmMinM) && act_dtype != LOWBIT_F32;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_qmm) return run_qmm(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
+  return run_qmv(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
+}
+
+lowbit_status lowbit_linear(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                            const void* scales, const void* zeros, const void* bias, void* y,
+                            int bits, int group, int64_t M, int64_t N, int64_t K, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return lowbit_linear_path(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K,
+                            workspace, workspace_bytes, LOWBIT_PATH_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+"""Python binding of the C ABI in include/lowbit.h (ctypes, argument marshalling only).
+
+Every step of the computation runs in the HIP library liblowbit.so; this module
+only turns torch tensors into device pointers and sizes, allocates outputs with
+torch when the caller does not pass them, and raises LowbitError on a non-OK
+status.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "liblowbit.so"
+
+LOWBIT_OK = 0
+STATUS_NAMES = {
+    0: "LOWBIT_OK", 1: "LOWBIT_ERR_INVALID_ARG", 2: "LOWBIT_ERR_UNSUPPORTED",
+    3: "LOWBIT_ERR_MISALIGNED", 4: "LOWBIT_ERR_NONFINITE", 5: "LOWBIT_ERR_RANGE",
+    6: "LOWBIT_ERR_WORKSPACE", 7: "LOWBIT_ERR_HIP",
+}
+LOWBIT_F32, LOWBIT_F16, LOWBIT_BF16 = 0, 1, 2
+PATH_AUTO, PATH_QMV, PATH_QMM = 0, 1, 2
+_DTYPE_ENUM = {torch.float32: LOWBIT_F32, torch.float16: LOWBIT_F16, torch.bfloat16: LOWBIT_BF16}
+_ENUM_DTYPE = {v: k for k, v in _DTYPE_ENUM.items()}
+
+EXPORTED_SYMBOLS = (
+    "lowbit_abi_version", "lowbit_packed_bytes", "lowbit_num_groups", "lowbit_quantize_pack",
+    "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path",
+    "lowbit_status_string", "lowbit_last_error",
+)
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{func}: {self.status_name}: {detail}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.environ.get("LOWBIT_LIBRARY", os.path.join(_PKG, _LIB_NAME))
+
+
+def load() -> ctypes.CDLL:
+    """Load liblowbit.so (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           f"(build it with __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    c_i64, c_sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.lowbit_abi_version.restype = ctypes.c_int
+    lib.lowbit_abi_version.argtypes = []
+    lib.lowbit_packed_bytes.restype = c_sz
+    lib.lowbit_packed_bytes.argtypes = [ctypes.c_int, c_i64, c_i64]
+    lib.lowbit_num_groups.restype = c_i64
+    lib.lowbit_num_groups.argtypes = [c_i64, ctypes.c_int]
+    lib.lowbit_quantize_pack.restype = ctypes.c_int
+    lib.lowbit_quantize_pack.argtypes = [vp, ctypes.c_int, ctypes.c_int, c_i64, c_i64, ctypes.c_int,
+                                         vp, vp, vp, vp, vp]
+    lib.lowbit_linear_workspace_bytes.restype = c_sz
+    lib.lowbit_linear_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, c_i64, c_i64, c_i64,
+                                                  ctypes.c_int]
+    lin = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, c_i64, c_i64, c_i64,
+           vp, c_sz]
+    lib.lowbit_linear.restype = ctypes.c_int
+    lib.lowbit_linear.argtypes = lin + [vp]
+    lib.lowbit_linear_path.restype = ctypes.c_int
+    lib.lowbit_linear_path.argtypes = lin + [ctypes.c_int, vp]
+    lib.lowbit_status_string.restype = ctypes.c_char_p
+    lib.lowbit_status_string.argtypes = [ctypes.c_int]
+    lib.lowbit_last_error.restype = ctypes.c_char_p
+    lib.lowbit_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != LOWBIT_OK:
+        detail = load().lowbit_last_error().decode(errors="replace")
+        raise LowbitError(status, func, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(device: torch.device, stream) -> Optional[int]:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if device.type != "cuda":
+        return None
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_cuda(*tensors: Optional[torch.Tensor]) -> None:
+    for t in tensors:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("lowbit tensors must live in GPU memory (device 'cuda')")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("lowbit tensors must be contiguous")
+
+
+# ---------------------------------------------------------------- C calls --
+
+def lowbit_abi_version() -> int:
+    return load().lowbit_abi_version()
+
+
+def lowbit_packed_bytes(bits: int, N: int, K: int) -> int:
+    return load().lowbit_packed_bytes(bits, N, K)
+
+
+def lowbit_num_groups(K: int, group: int) -> int:
+    return load().lowbit_num_groups(K, group)
+
+
+def lowbit_linear_workspace_bytes(bits: int, group: int, M: int, N: int, K: int,
+                                  act_dtype: torch.dtype) -> int:
+    return load().lowbit_linear_workspace_bytes(bits, group, M, N, K, _DTYPE_ENUM[act_dtype])
+
+
+def lowbit_status_string(status: int) -> str:
+    return load().lowbit_status_string(status).decode()
+
+
+def lowbit_last_error() -> str:
+    return load().lowbit_last_error().decode(errors="replace")
+
+
+def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch.dtype,
+                         want_codes: bool = False, out: Optional[Tuple] = None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor,
+                                               Optional[torch.Tensor]]:
+    """Quantize fp32 w[N, K] on the GPU.  Returns (packed, scales, zeros, codes|None).
+
+    `out` may give preallocated (packed, scales, zeros, codes) tensors.
+    """
+    lib = load()
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if out is None:
+        nbytes = lib.lowbit_packed_bytes(bits, N, K)
+        G = lib.lowbit_num_groups(K, group)
+        dev = w.device
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)[:nbytes].view(N, -1) \
+            if nbytes else torch.empty(0, dtype=torch.uint8, device=dev)
+        scales = torch.empty((N, max(G, 0)), dtype=sz_dtype, device=dev)
+        zeros = torch.empty((N, max(G, 0)), dtype=sz_dtype, device=dev)
+        codes = torch.empty((N, K), dtype=torch.uint8, device=dev) if want_codes else None
+    else:
+        packed, scales, zeros, codes = out
+    _require_cuda(w, packed, scales, zeros, codes)
+    st = lib.lowbit_quantize_pack(_ptr(w), bits, group, N, K, _DTYPE_ENUM[sz_dtype], _ptr(scales),
+                                  _ptr(zeros), _ptr(packed), _ptr(codes),
+                                  _stream_handle(w.device, stream))
+    _check(st, "lowbit_quantize_pack")
+    return packed, scales, zeros, codes
+
+
+def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                  bias: Optional[torch.Tensor], bits: int, group: int,
+                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  path: Optional[int] = None, stream=None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . dequant(packed, scales, zeros)^T (+ bias), on the GPU."""
+    lib = load()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    N = scales.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _require_cuda(x, packed, scales, zeros, bias, y, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(x), _DTYPE_ENUM[x.dtype], _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(bias),
+            _ptr(y), bits, group, M, N, K, _ptr(workspace), ws_bytes)
+    s = _stream_handle(x.device, stream)
+    if path is None:
+        st = lib.lowbit_linear(*args, s)
+        _check(st, "lowbit_linear")
+    else:
+        st = lib.lowbit_linear_path(*args, int(path), s)
+        _check(st, "lowbit_linear_path")
+    return y

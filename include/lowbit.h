@@ -1,0 +1,163 @@
+/*
+ * lowbit.h -- C ABI of the groupwise weight-only low-bit linear layer for
+ * AMD MI355X (gfx950).
+ *
+ *   y[M, N] = x[M, K] . dequant(Wq)[N, K]^T (+ bias[N])
+ *   dequant(Wq)[n, k] = s[n, k / group] * q[n, k] + z[n, k / group]
+ *
+ * The operation and its weight format come from these pages:
+ *   - "Add torchao mps ops": the linear:afpwx scheme -- weights only, quantized
+ *     groupwise with a bit width of 1..7 and a group size of 32, 64, 128 or 256;
+ *     activations stay floating point.
+ *   - "metal lowbit kernels: qmv_fast optimization", Summary: scales and zeros
+ *     are consumed N x num_groups (as the quantize function produces them), and
+ *     codes are stored contiguously, carrying over into the next byte when the
+ *     current byte is full.  The same page's closing question -- whether the
+ *     decode matrix-vector approach also serves a matrix-matrix product -- is
+ *     answered here by a separate MFMA path for larger M.
+ *   - "Revamp int4 MPS support in torchao": the layer must accept a bias.
+ *   - "Add support for fbgemm int4 mm kernel": configuration is passed as
+ *     integers and enums, not strings (the review comment on that page).
+ *
+ * Conventions fixed where the pages are silent:
+ *   - dequantization is w = s*q + z; z is a real-valued offset stored in the
+ *     same dtype as s (the activation dtype);
+ *   - quantization is asymmetric min/max per (row, group):
+ *       s = (max - min) / (2^b - 1), z = min (a zero min/max counts as +0),
+ *       s and z are rounded to their storage dtype (nearest even) first, then
+ *       q = clamp(rint_half_even((w - z) / s), 0, 2^b - 1) in fp32 with a
+ *       correctly rounded divide, and q = 0 where the stored s is 0;
+ *   - packing: row n occupies bytes [n*K*b/8, (n+1)*K*b/8) of `packed`; bit j
+ *     of code q[n,k] is bit (p & 7) of byte (p >> 3) of that row, p = k*b + j
+ *     (least significant bit first), no padding.
+ *
+ * Memory: every pointer argument other than `stream` and the host-side helpers
+ * is a DEVICE pointer owned by the caller; the library never keeps a pointer
+ * after a call returns.  The library allocates one small per-device status
+ * word for lowbit_quantize_pack on first use and nothing else.
+ *
+ * Errors: arguments are validated on the host before any HIP call, so every
+ * LOWBIT_ERR_INVALID_ARG / UNSUPPORTED / MISALIGNED / WORKSPACE result can be
+ * produced without a GPU.  A failed HIP call yields LOWBIT_ERR_HIP; the text of
+ * the last error on the calling thread is available from lowbit_last_error().
+ * No C++ exception crosses this interface.
+ */
+#ifndef LOWBIT_H_
+#define LOWBIT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWBIT_ABI_VERSION 1
+
+typedef enum lowbit_status {
+  LOWBIT_OK = 0,
+  LOWBIT_ERR_INVALID_ARG = 1,  /* bits/group/shape out of range, NULL pointer      */
+  LOWBIT_ERR_UNSUPPORTED = 2,  /* a dtype or path combination that is not built     */
+  LOWBIT_ERR_MISALIGNED = 3,   /* packed not 16-byte aligned, or an array not
+                                  aligned to its element size                       */
+  LOWBIT_ERR_NONFINITE = 4,    /* quantize: the weight holds a NaN or an infinity   */
+  LOWBIT_ERR_RANGE = 5,        /* quantize: a scale or zero overflows its dtype     */
+  LOWBIT_ERR_WORKSPACE = 6,    /* workspace pointer/size inconsistent               */
+  LOWBIT_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed        */
+} lowbit_status;
+
+typedef enum lowbit_dtype {
+  LOWBIT_F32 = 0,
+  LOWBIT_F16 = 1,
+  LOWBIT_BF16 = 2
+} lowbit_dtype;
+
+/* Which kernel family lowbit_linear_path runs. */
+typedef enum lowbit_path {
+  LOWBIT_PATH_AUTO = 0,  /* qmv for M < 16 or fp32 activations, qmm otherwise */
+  LOWBIT_PATH_QMV = 1,   /* decode matrix-vector kernel, any M              */
+  LOWBIT_PATH_QMM = 2    /* MFMA matrix-matrix kernel, fp16/bf16 only       */
+} lowbit_path;
+
+/* ABI version of the loaded library (LOWBIT_ABI_VERSION at build time). */
+int lowbit_abi_version(void);
+
+/* Bytes of one packed weight matrix: N*K*bits/8.  Returns 0 when bits is not
+ * in 1..7, N or K is not positive, or K is not a multiple of 32. */
+size_t lowbit_packed_bytes(int bits, int64_t N, int64_t K);
+
+/* K / group, or 0 when group is not 32/64/128/256 or K is not a positive
+ * multiple of group. */
+int64_t lowbit_num_groups(int64_t K, int group);
+
+/* Quantize and pack a weight matrix (one-off, not on the decode path).
+ *
+ *   w        device, fp32, N x K row-major (the linear weight, [out, in]).
+ *   bits     1..7;  group: 32, 64, 128 or 256;  K % group == 0;  N, K > 0.
+ *   sz_dtype storage dtype of scales and zeros; use the activation dtype that
+ *            lowbit_linear will be called with.
+ *   scales   device, N x (K/group) row-major, sz_dtype.  Written.
+ *   zeros    device, N x (K/group) row-major, sz_dtype.  Written.
+ *   packed   device, lowbit_packed_bytes(bits, N, K) bytes, 16-byte aligned.
+ *            Written (every byte).
+ *   codes    device, N x K bytes holding one code per byte, or NULL.
+ *   stream   hipStream_t (NULL = the default stream).
+ *
+ * The call enqueues the work on `stream` and then waits for that stream,
+ * because it reports data-dependent errors: LOWBIT_ERR_NONFINITE if w holds a
+ * NaN or infinity, LOWBIT_ERR_RANGE if a scale or zero is not finite in
+ * sz_dtype.  On either error the output buffers hold unspecified values. */
+lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t N, int64_t K,
+                                   lowbit_dtype sz_dtype, void* scales, void* zeros,
+                                   uint8_t* packed, uint8_t* codes, void* stream);
+
+/* Bytes of workspace that lowbit_linear / lowbit_linear_path can use for the
+ * given problem (0 when no schedule needs one).  A call given less than this
+ * (including NULL / 0) falls back to a schedule without workspace. */
+size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, int64_t K,
+                                     lowbit_dtype act_dtype);
+
+/* y = x . dequant(packed, scales, zeros)^T (+ bias), enqueued on `stream`
+ * (asynchronous: the call returns once the kernels are launched).
+ *
+ *   x        device, M x K row-major, act_dtype.
+ *   packed, scales, zeros   as written by lowbit_quantize_pack with
+ *            sz_dtype == act_dtype (or built by the caller in that format).
+ *   bias     device, N elements of act_dtype, or NULL for no bias.
+ *   y        device, M x N row-major, act_dtype.  Overwritten; must not alias
+ *            any input.
+ *   M >= 0 (M == 0 is a no-op that returns LOWBIT_OK; x and y may then be
+ *   NULL), N > 0, K > 0,
+ *   K % group == 0.
+ *   workspace/workspace_bytes: device scratch or NULL/0.  When non-NULL it
+ *            must be 256-byte aligned and zero-filled before its first use;
+ *            every call leaves it zero-filled again.  Calls that run
+ *            concurrently must not share one workspace.
+ *
+ * Products accumulate in fp32; the bias is added in fp32 and the result is
+ * rounded to act_dtype to nearest even.  Identical inputs give bitwise
+ * identical outputs (no floating-point atomics). */
+lowbit_status lowbit_linear(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                            const void* scales, const void* zeros, const void* bias, void* y,
+                            int bits, int group, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* lowbit_linear with an explicit kernel family.  LOWBIT_PATH_QMM with fp32
+ * activations returns LOWBIT_ERR_UNSUPPORTED. */
+lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                                 const void* scales, const void* zeros, const void* bias, void* y,
+                                 int bits, int group, int64_t M, int64_t N, int64_t K,
+                                 void* workspace, size_t workspace_bytes, lowbit_path path,
+                                 void* stream);
+
+/* Static text for a status code. */
+const char* lowbit_status_string(lowbit_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* lowbit_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H_ */

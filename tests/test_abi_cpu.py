@@ -1,0 +1,103 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and
+rejects bad arguments before touching the HIP runtime (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_groupwise_weight_amd import lowbit as lb
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "lowbit.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 6
+F32, F16, BF16 = 0, 1, 2
+A = 0x10000          # a fake, 256-byte aligned "device" address: never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lowbit_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(lb.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lowbit_lib):
+    for name in declared_functions():
+        assert hasattr(lowbit_lib, name), name
+    assert lowbit_lib.lowbit_abi_version() == 1
+
+
+def test_size_helpers(lowbit_lib):
+    assert lb.lowbit_packed_bytes(4, 4096, 4096) == 4096 * 4096 // 2
+    assert lb.lowbit_packed_bytes(3, 10, 96) == 10 * 96 * 3 // 8
+    assert lb.lowbit_packed_bytes(8, 10, 96) == 0
+    assert lb.lowbit_packed_bytes(3, 10, 100) == 0
+    assert lb.lowbit_num_groups(4096, 64) == 64
+    assert lb.lowbit_num_groups(4096, 48) == 0
+    assert lb.lowbit_num_groups(100, 32) == 0
+    assert lb.lowbit_linear_workspace_bytes(4, 64, 1, 4096, 4096, __import__("torch").float16) >= 0
+
+
+def lin(lib, **kw):
+    a = dict(x=A, act=F16, packed=A, scales=A, zeros=A, bias=None, y=A, bits=4, group=64, M=1,
+             N=64, K=256, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.lowbit_linear(a["x"], a["act"], a["packed"], a["scales"], a["zeros"], a["bias"],
+                             a["y"], a["bits"], a["group"], a["M"], a["N"], a["K"], a["ws"],
+                             a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=0), INVALID), (dict(bits=8), INVALID), (dict(group=48), INVALID),
+    (dict(group=16), INVALID), (dict(K=96, group=64), INVALID), (dict(N=0), INVALID),
+    (dict(K=0), INVALID), (dict(M=-1), INVALID), (dict(x=None), INVALID),
+    (dict(packed=None), INVALID), (dict(scales=None), INVALID), (dict(y=None), INVALID),
+    (dict(act=7), UNSUPPORTED), (dict(packed=A + 8), MISALIGNED), (dict(x=A + 4), MISALIGNED),
+    (dict(y=A + 1), MISALIGNED), (dict(ws=None, ws_bytes=64), WORKSPACE),
+    (dict(ws=A + 16, ws_bytes=64), WORKSPACE),
+    (dict(M=0), OK),   # M == 0 is a no-op that never reaches the runtime
+    (dict(M=0, x=None, y=None), OK), (dict(M=0, packed=None), INVALID),
+])
+def test_linear_validation(lowbit_lib, kw, status):
+    assert lin(lowbit_lib, **kw) == status
+    if status != OK:
+        assert lb.lowbit_last_error() != ""
+
+
+def test_qmm_path_rejects_fp32(lowbit_lib):
+    st = lowbit_lib.lowbit_linear_path(A, F32, A, A, A, None, A, 4, 64, 32, 64, 256, None, 0, 2,
+                                       None)
+    assert st == UNSUPPORTED
+    st = lowbit_lib.lowbit_linear_path(A, F16, A, A, A, None, A, 4, 64, 0, 64, 256, None, 0, 9,
+                                       None)
+    assert st == INVALID
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(bits=9), INVALID), (dict(group=100), INVALID), (dict(K=48, group=32), INVALID),
+    (dict(w=None), INVALID), (dict(packed=A + 4), MISALIGNED), (dict(w=A + 4), MISALIGNED),
+    (dict(sz=5), UNSUPPORTED), (dict(N=-3), INVALID),
+])
+def test_quantize_validation(lowbit_lib, args, status):
+    a = dict(w=A, bits=4, group=32, N=8, K=64, sz=F16, scales=A, zeros=A, packed=A, codes=None)
+    a.update(args)
+    st = lowbit_lib.lowbit_quantize_pack(a["w"], a["bits"], a["group"], a["N"], a["K"], a["sz"],
+                                         a["scales"], a["zeros"], a["packed"], a["codes"], None)
+    assert st == status
+
+
+def test_status_strings(lowbit_lib):
+    for s in range(8):
+        assert lb.lowbit_status_string(s)
+    assert lb.lowbit_status_string(99) == "unknown status"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(lb, "_lib", None)
+    monkeypatch.setenv("LOWBIT_LIBRARY", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        lb.load()
