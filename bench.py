@@ -88,6 +88,7 @@ def prepare(case, copies, dev):
 
 
 def launch(p, i, stream):
+    """One lowbit_linear call on weight copy i (mod copies)."""
     from bit_groupwise_weight_amd import lowbit as lb
     c = p["case"]
     packed, s, z = p["sets"][i % len(p["sets"])]
@@ -95,9 +96,33 @@ def launch(p, i, stream):
                      stream=stream)
 
 
-def time_kernel(p, reps, stream):
-    """Average time of one launch over `reps` back-to-back launches (rotating
-    weight copies), from HIP events recorded on the launch stream."""
+def capture(fn, n, stream):
+    """A HIP graph holding fn(0), ..., fn(n-1), captured on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream()
+        for i in range(n):
+            fn(i, s)
+    return g
+
+
+def time_graph(g, replays, per_replay, stream):
+    """Microseconds per unit of work: HIP events around `replays` replays of a
+    graph holding `per_replay` units, recorded on the replay stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * per_replay)
+
+
+def time_eager(p, reps, stream):
+    """Microseconds per call when launched one by one from Python (host-bound)."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     for i in range(3):
@@ -107,7 +132,7 @@ def time_kernel(p, reps, stream):
         launch(p, i, stream)
     e1.record(stream)
     e1.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps   # microseconds
+    return e0.elapsed_time(e1) * 1e3 / reps
 
 
 def cpu_baseline(cases, reps):
@@ -161,30 +186,46 @@ def main():
     mp = [prepare(c, copies_qmm, dev) for c in mcases]
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, s):
         for p in qp:
-            launch(p, i, stream)
+            launch(p, i, s)
         for p in mp:
-            launch(p, i, stream)
+            launch(p, i, s)
 
     for i in range(args.warmup):
-        step(i)
+        step(i, stream)
+    torch.cuda.synchronize()
+
+    # One graph per rotating copy set; each holds one full step.
+    copies = min(copies_qmv, copies_qmm)
+    step_graphs = [capture(lambda j, s, c=c: step(c, s), 1, stream) for c in range(copies)]
+    torch.cuda.synchronize()
+    for g in step_graphs:
+        g.replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step_graphs[i % copies].replay()
     e1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host wall {wall_ms:.1f} ms)")
+    log(f"timed {args.steps} steps (graph replay): {ms_per_step:.4f} ms/step "
+        f"(host wall {wall_ms:.1f} ms)")
 
-    # per-kernel average launch durations (HIP events on the launch stream)
-    qmv_us = [time_kernel(p, args.reps, stream) for p in qp]
-    qmm_us = [time_kernel(p, args.reps, stream) for p in mp]
+    # Per-kernel average launch durations: a graph of back-to-back launches
+    # over all rotating copies, replayed; HIP events on the replay stream.
+    def kernel_us(p):
+        n = len(p["sets"])
+        g = capture(lambda i, s: launch(p, i, s), n, stream)
+        return time_graph(g, max(1, args.reps // n + 1), n, stream)
+
+    qmv_us = [kernel_us(p) for p in qp]
+    qmm_us = [kernel_us(p) for p in mp]
+    eager_us = [time_eager(p, args.reps, stream) for p in qp]
     per_bit = []
     for c, us in zip(qcases, qmv_us):
         gbps = algo_bytes(c) / (us * 1e-6) / 1e9
@@ -242,8 +283,10 @@ def main():
             "traffic": None,
         },
         "qmm": qmm,
-        "timing": "per-kernel us = HIP-event time of a loop of back-to-back launches on the "
-                  "launch stream / launches",
+        "qmv_eager_us_per_call": [round(u, 3) for u in eager_us],
+        "timing": "per-kernel us = HIP-event time of replays of a HIP graph of back-to-back "
+                  "launches (rotating weight copies) / launches; steps replay one graph per "
+                  "step; qmv_eager_us_per_call = one Python call per launch (host-bound)",
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline ...")

@@ -104,4 +104,24 @@ template <> struct Magic<ACT_BF16> {
   static constexpr float value = 128.0f;
 };
 
+// ---- cross-lane sums with DPP ----------------------------------------------
+// x + (x moved by a DPP pattern); lanes outside row_mask add 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+  return x + __int_as_float(moved);
+}
+
+// Sum over aligned groups of `lanes` lanes (1, 2, ..., 64; uniform).  The
+// group's total ends up in its LAST lane (lane % lanes == lanes - 1).
+__device__ __forceinline__ float group_sum_to_last(float x, int lanes) {
+  if (lanes >= 2) x = dpp_add<0xb1>(x);          // quad_perm [1,0,3,2]
+  if (lanes >= 4) x = dpp_add<0x4e>(x);          // quad_perm [2,3,0,1]
+  if (lanes >= 8) x = dpp_add<0x141>(x);         // row_half_mirror
+  if (lanes >= 16) x = dpp_add<0x140>(x);        // row_mirror
+  if (lanes >= 32) x = dpp_add<0x142, 0xa>(x);   // row_bcast15 into rows 1 and 3
+  if (lanes >= 64) x = dpp_add<0x143, 0x8>(x);   // row_bcast31 into row 3
+  return x;
+}
+
 }  // namespace lowbit

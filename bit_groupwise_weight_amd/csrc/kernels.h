@@ -36,10 +36,11 @@ struct QmvParams {
   int groups;             // K / group
   int64_t row_bytes;      // K * bits / 8
   int aligned16;          // row_bytes % 16 == 0 (every row starts 16-byte aligned)
+  int sz_vec;             // K % 128 == 0: a unit's scales/zeros are one aligned vector
 };
 struct QmvLaunch {
   dim3 grid, block;
-  int mt;                 // activation rows per pass: 1 or 4
+  int mt;                 // activation rows per pass: 1, 2 or 4
 };
 // One entry point per bit width (compiled as separate objects).
 hipError_t launch_qmv_b1(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
@@ -49,6 +50,14 @@ hipError_t launch_qmv_b4(const QmvParams&, const QmvLaunch&, int group, int act,
 hipError_t launch_qmv_b5(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
 hipError_t launch_qmv_b6(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
 hipError_t launch_qmv_b7(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+// LDS bytes the decode kernel stages per activation row and per unit of a round.
+int qmv_stage_bytes_b1(int act);
+int qmv_stage_bytes_b2(int act);
+int qmv_stage_bytes_b3(int act);
+int qmv_stage_bytes_b4(int act);
+int qmv_stage_bytes_b5(int act);
+int qmv_stage_bytes_b6(int act);
+int qmv_stage_bytes_b7(int act);
 
 // --------------------------------------------------------------------- qmm --
 struct QmmParams {

@@ -8,6 +8,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -99,6 +100,24 @@ const QmvLauncher kQmv[8] = {nullptr,
 
 constexpr int64_t kQmmMinM = 16;
 
+typedef int (*QmvStageBytes)(int);
+const QmvStageBytes kQmvStage[8] = {nullptr,
+                                    lowbit::qmv_stage_bytes_b1,
+                                    lowbit::qmv_stage_bytes_b2,
+                                    lowbit::qmv_stage_bytes_b3,
+                                    lowbit::qmv_stage_bytes_b4,
+                                    lowbit::qmv_stage_bytes_b5,
+                                    lowbit::qmv_stage_bytes_b6,
+                                    lowbit::qmv_stage_bytes_b7};
+
+// LDS budget of one decode block for its staged activations.
+constexpr int64_t kQmvStageBudget = 64 * 1024 - 256;  // minus one scratch run
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
 lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
                       const void* zeros, const void* bias, void* y, int bits, int group,
                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -111,21 +130,32 @@ lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, co
   p.groups = static_cast<int>(K / group);
   p.row_bytes = K * bits / 8;
   p.aligned16 = (p.row_bytes % 16) == 0;
+  p.sz_vec = (K % 128) == 0;
   int shift = 0;
   while ((1 << shift) < p.units && shift < 6) ++shift;
   p.lpr_shift = shift;
+  const int lanes = 1 << shift;
 
+  // Activation rows per pass: as many as fit the LDS stage (at most 4).
   lowbit::QmvLaunch l{};
-  l.mt = (M == 1) ? 1 : 4;
+  const int64_t per_row = static_cast<int64_t>(kQmvStage[bits](act_kind(act))) * lanes;
+  l.mt = 1;
+  if (M >= 2 && 2 * per_row <= kQmvStageBudget) l.mt = 2;
+  if (M >= 3 && 4 * per_row <= kQmvStageBudget) l.mt = 4;
+  if (per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
   const int R = (l.mt == 1) ? 2 : 1;
-  // Prefer 256-thread blocks; shrink them when that leaves too few blocks to
-  // cover the chip.
-  int threads = 256;
+
+  // Block size: 256 threads unless that leaves fewer than ~2 blocks per CU.
+  int threads = env_int("LOWBIT_QMV_BLOCK", 0);
   auto blocks_for = [&](int t) {
     const int64_t rows_per_block = static_cast<int64_t>(t >> shift) * R;
     return (N + rows_per_block - 1) / rows_per_block;
   };
-  while (threads > 64 && blocks_for(threads) < 1024 && (threads >> 1) >= (1 << shift)) threads >>= 1;
+  if (threads != 64 && threads != 128 && threads != 256) {
+    threads = 256;
+    while (threads > 128 && blocks_for(threads) < 512 && (threads >> 1) >= lanes) threads >>= 1;
+  }
+  if (threads < lanes) threads = lanes;
   const int64_t bx = blocks_for(threads);
   const int64_t by = (M + l.mt - 1) / l.mt;
   if (bx > 0x7fffffff || by > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "problem too large");

@@ -2,24 +2,27 @@
 //
 // Prior art: the qmv_fast Metal kernel of "metal lowbit kernels: qmv_fast
 // optimization" (Summary) streams packed rows and applies the N x num_groups
-// scales and zeros in the inner loop.  This kernel keeps that idea and is laid
-// out for CDNA4:
+// scales and zeros inside the dot product.  This kernel keeps that idea and is
+// laid out for CDNA4:
 //   * a row's codes are cut into 128-code units; a unit of b-bit codes is
 //     exactly b x 16 bytes, fetched with b 128-bit loads;
-//   * 2^lpr_shift lanes of one wavefront share a group of R rows, each lane
-//     walking units u = lane, lane + lanes, ...; the lane holds the activation
-//     slice of its unit in registers and reuses it for all R rows;
-//   * codes are unpacked in registers; for fp16/bf16 activations two codes are
-//     OR-ed into the mantissas of a 16-bit pair (value MAGIC + q, exact) and
-//     multiplied into an fp32 accumulator with one dot2 instruction; the MAGIC
-//     offset is removed per 32-code run with the run's activation sum X:
-//       sum x*q = P - MAGIC * X
-//   * per 32-code run (which never crosses a group): y += s*(sum x*q) + z*X,
-//     i.e. sum_k x_k (s q_k + z) without forming the dequantized weight;
-//   * partial sums of the lanes of a row group are combined with lane
-//     shuffles, then bias is added in fp32 and the result rounded once.
+//   * 2^lpr_shift lanes of a wavefront share a group of R rows; in round t
+//     lane l owns unit t*lanes + l of each of its R rows;
+//   * the block stages the activations of the round once in LDS, already
+//     rearranged into the operand pairs the unpack plan needs, together with
+//     each 32-code run's activation sum X and constant part C; activation
+//     loads are issued before the weight loads so the stage is ready while the
+//     weights are still in flight;
+//   * fp16: codes become fp16 values by OR-ing exponent fields (see
+//     qmv_plan.h) and are multiplied in pairs by v_dot2_f32_f16; bf16 uses the
+//     same trick with the fixed constant 128; fp32 converts each code;
+//   * per 32-code run (which never crosses a group):
+//       y += s * (sum_k x_k q_k) + z * X,  sum_k x_k q_k = P - C;
+//   * the R row partial sums of the lanes of a row group are combined with
+//     lane shuffles; bias is added in fp32 and the result rounded once.
 #include "device_common.h"
 #include "kernels.h"
+#include "qmv_plan.h"
 
 #ifndef LOWBIT_BITS
 #error "compile with -DLOWBIT_BITS=<1..7>"
@@ -27,58 +30,212 @@
 
 namespace lowbit {
 
-// Load the 16*BITS bytes of one 128-code unit of one row (or the leading
-// nsub 32-code runs of a ragged last unit) into 4*BITS words.
-template <int BITS>
-__device__ __forceinline__ void load_unit(const uint8_t* rowp, bool vec16, int nsub,
-                                          uint32_t (&d)[4 * BITS]) {
-  if (vec16) {
+// Raw activation words per 32-code run and staged words per run.
+template <int ACT> struct RawWords { static constexpr int n = (ACT == ACT_F32) ? 32 : 16; };
+template <int ACT, int BITS> struct StagedWords;
+template <int BITS> struct StagedWords<ACT_F16, BITS> { static constexpr int n = F16Plan<BITS>::n; };
+template <int BITS> struct StagedWords<ACT_BF16, BITS> { static constexpr int n = 16; };
+template <int BITS> struct StagedWords<ACT_F32, BITS> { static constexpr int n = 32; };
+// uint4 quads per staged run: the words, then X and C, padded to 16 bytes.
+template <int ACT, int BITS> struct RunQuads {
+  static constexpr int n = (StagedWords<ACT, BITS>::n + 2 + 3) / 4;
+};
+
+// ---------------------------------------------------------------- staging --
+
+template <int ACT, int BITS, int I = 0>
+__device__ __forceinline__ void f16_stage_slots(const uint32_t* raw, uint32_t* out, float& C) {
+  if constexpr (I < F16Plan<BITS>::n) {
+    constexpr PairSlot s = F16Plan<BITS>::table.s[I];
+    uint32_t lo = 0, hi = 0;
+    if constexpr (s.klo >= 0) lo = (raw[s.klo >> 1] >> ((s.klo & 1) * 16)) & 0xffffu;
+    if constexpr (s.khi >= 0) hi = (raw[s.khi >> 1] >> ((s.khi & 1) * 16)) & 0xffffu;
+    const uint32_t w = lo | (hi << 16);
+    out[I] = w;
+    constexpr uint32_t mag = f16_magic_for_offset(s.olo) | (f16_magic_for_offset(s.ohi) << 16);
+    C = dot2<ACT_F16>(w, mag, C);
+    f16_stage_slots<ACT, BITS, I + 1>(raw, out, C);
+  }
+}
+
+// Turn 32 raw activations into the staged words of one run (+ X, C).
+template <int ACT, int BITS>
+__device__ __forceinline__ void stage_run(const uint32_t* raw, uint32_t* out) {
+  constexpr int W = StagedWords<ACT, BITS>::n;
+  float X = 0.0f, C = 0.0f;
+  if constexpr (ACT == ACT_F32) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) { out[i] = raw[i]; X += __uint_as_float(raw[i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) X = dot2<ACT>(raw[i], Magic<ACT>::ones, X);
+    if constexpr (ACT == ACT_F16) {
+      f16_stage_slots<ACT, BITS>(raw, out, C);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out[i] = raw[i];
+      C = Magic<ACT>::value * X;
+    }
+  }
+  out[W] = __float_as_uint(X);
+  out[W + 1] = __float_as_uint(C);
+#pragma unroll
+  for (int i = W + 2; i < RunQuads<ACT, BITS>::n * 4; ++i) out[i] = 0u;
+}
+
+// ------------------------------------------------------------------ dots --
+
+// The value unchanged, but held in a VGPR and opaque to constant folding.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+template <int BITS, int I = 0>
+__device__ __forceinline__ float f16_dot_slots(const uint32_t* w, const uint32_t* xs, float acc) {
+  if constexpr (I < F16Plan<BITS>::n) {
+    constexpr PairSlot s = F16Plan<BITS>::table.s[I];
+    uint32_t win;
+    if constexpr (s.shift == 0) {
+      win = w[s.word];
+    } else if constexpr (s.word + 1 < BITS) {
+      win = __builtin_amdgcn_alignbit(w[s.word + 1], w[s.word], s.shift);
+    } else {
+      win = w[s.word] >> s.shift;
+    }
+    constexpr uint32_t m = (1u << BITS) - 1u;
+    constexpr uint32_t mask = (s.klo >= 0 ? (m << s.olo) : 0u) |
+                              (s.khi >= 0 ? (m << (16 + s.ohi)) : 0u);
+    constexpr uint32_t mag = f16_magic_for_offset(s.olo) | (f16_magic_for_offset(s.ohi) << 16);
+    // mag lives in a VGPR so that the AND and the OR fuse into one
+    // v_and_or_b32 (a VOP3 form may read one scalar constant: the mask)
+    acc = dot2<ACT_F16>(xs[I], (win & mask) | in_vgpr(mag), acc);
+    return f16_dot_slots<BITS, I + 1>(w, xs, acc);
+  } else {
+    return acc;
+  }
+}
+
+template <int BITS, int I = 0>
+__device__ __forceinline__ float bf16_dot_pairs(const uint32_t* w, const uint32_t* xs, float acc) {
+  if constexpr (I < 16) {
+    const uint32_t h = code_at<BITS, 2 * I>(w) | (code_at<BITS, 2 * I + 1>(w) << 16) |
+                       Magic<ACT_BF16>::pair;
+    acc = dot2<ACT_BF16>(xs[I], h, acc);
+    return bf16_dot_pairs<BITS, I + 1>(w, xs, acc);
+  } else {
+    return acc;
+  }
+}
+
+template <int BITS, int I = 0>
+__device__ __forceinline__ float f32_dot(const uint32_t* w, const uint32_t* xs, float acc) {
+  if constexpr (I < 32) {
+    acc = __builtin_fmaf(__uint_as_float(xs[I]), static_cast<float>(code_at<BITS, I>(w)), acc);
+    return f32_dot<BITS, I + 1>(w, xs, acc);
+  } else {
+    return acc;
+  }
+}
+
+// sum_k x_k q_k over one run, from the staged words and the run's code words.
+template <int ACT, int BITS>
+__device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) {
+  constexpr int W = StagedWords<ACT, BITS>::n;
+  if constexpr (ACT == ACT_F16) {
+    return f16_dot_slots<BITS>(w, xs, 0.0f) - __uint_as_float(xs[W + 1]);
+  } else if constexpr (ACT == ACT_BF16) {
+    return bf16_dot_pairs<BITS>(w, xs, 0.0f) - __uint_as_float(xs[W + 1]);
+  } else {
+    return f32_dot<BITS>(w, xs, 0.0f);
+  }
+}
+
+// ----------------------------------------------------------------- loads --
+
+// The 4*BITS words of 128-code unit `u` of one row.  FAST: the unit is whole
+// and 16-byte aligned (b 128-bit loads).  Otherwise runs past the row end
+// (nsub of them are valid) re-read the last valid run and are zeroed.
+template <int BITS, bool FAST>
+__device__ __forceinline__ void load_unit(const uint8_t* rowp, int nsub, uint32_t (&d)[4 * BITS]) {
+  if constexpr (FAST) {
     const uint4* s = reinterpret_cast<const uint4*>(rowp);
 #pragma unroll
     for (int i = 0; i < BITS; ++i) {
-      uint4 v = s[i];
+      const uint4 v = s[i];
       d[4 * i + 0] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
     }
   } else {
     const uint32_t* s = reinterpret_cast<const uint32_t*>(rowp);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int jj = min(j, nsub - 1);
 #pragma unroll
-      for (int i = 0; i < BITS; ++i) d[j * BITS + i] = (j < nsub) ? s[j * BITS + i] : 0u;
+      for (int i = 0; i < BITS; ++i) {
+        const uint32_t v = s[jj * BITS + i];
+        d[j * BITS + i] = (j < nsub) ? v : 0u;
+      }
     }
   }
 }
 
-// sum over 32 codes of x_k * (MAGIC + q_k), x given as 16 packed pairs.
-template <int BITS, int ACT, int I = 0>
-__device__ __forceinline__ float dot_run_pairs(const uint32_t* w, const uint32_t* xp, float acc) {
-  if constexpr (I < 16) {
-    const uint32_t c0 = code_at<BITS, 2 * I>(w);
-    const uint32_t c1 = code_at<BITS, 2 * I + 1>(w);
-    const uint32_t h = c0 | (c1 << 16) | Magic<ACT>::pair;
-    acc = dot2<ACT>(xp[I], h, acc);
-    return dot_run_pairs<BITS, ACT, I + 1>(w, xp, acc);
-  } else {
-    return acc;
+// 32 activations starting at element `off` (always a valid address); the
+// caller zeroes them when the run lies outside x.
+template <int ACT>
+__device__ __forceinline__ void load_raw_run(const void* x, int64_t off,
+                                             uint32_t (&raw)[RawWords<ACT>::n]) {
+  constexpr int Q = RawWords<ACT>::n / 4;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                    off * Act<ACT>::bytes);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint4 v = src[q];
+    raw[4 * q + 0] = v.x; raw[4 * q + 1] = v.y; raw[4 * q + 2] = v.z; raw[4 * q + 3] = v.w;
   }
 }
 
-// sum over 32 codes of x_k * q_k, x as fp32.
-template <int BITS, int I = 0>
-__device__ __forceinline__ float dot_run_f32(const uint32_t* w, const float* xf, float acc) {
-  if constexpr (I < 32) {
-    const float q = static_cast<float>(code_at<BITS, I>(w));
-    acc = __builtin_fmaf(xf[I], q, acc);
-    return dot_run_f32<BITS, I + 1>(w, xf, acc);
+// Raw bits of the scales (or zeros) of the 4 runs of unit u of one row; run j
+// uses group (u*128 + 32j) / GROUP.  FAST (K % 128 == 0): the unit's groups
+// are one aligned vector of max(1, 128/GROUP) elements.  Conversion to fp32
+// happens at first use, so these loads never force an early wait.
+template <int ACT, int GROUP, bool FAST>
+__device__ __forceinline__ void load_unit_sz(const void* base, int64_t row_off, int u, int groups,
+                                             uint32_t (&v)[4]) {
+  constexpr int NG = GROUP >= 128 ? 1 : 128 / GROUP;
+  using T = typename Act<ACT>::bits_t;
+  const T* p = static_cast<const T*>(base) + row_off;
+  if constexpr (FAST) {
+    const int g0 = GROUP == 256 ? (u >> 1) : u * NG;
+    T t[NG];
+    if constexpr (NG * sizeof(T) == 16) {
+      const uint4 a = *reinterpret_cast<const uint4*>(p + g0);
+      __builtin_memcpy(t, &a, 16);
+    } else if constexpr (NG * sizeof(T) == 8) {
+      const uint2 a = *reinterpret_cast<const uint2*>(p + g0);
+      __builtin_memcpy(t, &a, 8);
+    } else if constexpr (NG * sizeof(T) == 4) {
+      const uint32_t a = *reinterpret_cast<const uint32_t*>(p + g0);
+      __builtin_memcpy(t, &a, 4);
+    } else {
+      t[0] = p[g0];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = t[(j * 32) / GROUP % NG];
   } else {
-    return acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = p[min((u * 128 + 32 * j) / GROUP, groups - 1)];
   }
 }
 
-template <int BITS, int GROUP, int ACT, int MT>
+// ---------------------------------------------------------------- kernel --
+
+template <int BITS, int GROUP, int ACT, int MT, bool FAST>
 __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
+  extern __shared__ uint4 stage[];
   constexpr int R = (MT == 1) ? 2 : 1;          // rows per row group
-  constexpr int XW = (ACT == ACT_F32) ? 32 : 16; // words of x per 32-code run
+  constexpr int RAW = RawWords<ACT>::n;
+  constexpr int QD = RunQuads<ACT, BITS>::n;    // staged quads per run
+
   const int tid = threadIdx.x;
   const int lanes = 1 << p.lpr_shift;
   const int lane = tid & (lanes - 1);
@@ -86,6 +243,9 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   const int rgs = blockDim.x >> p.lpr_shift;
   const int n_base = (blockIdx.x * rgs + rg) * R;
   const int m0 = blockIdx.y * MT;
+  const int mcount = min(MT, p.M - m0);
+  const int nruns = MT * 4 * lanes;              // staged runs per round
+  const int rounds = (p.units + lanes - 1) / lanes;
 
   float acc[R][MT];
 #pragma unroll
@@ -93,83 +253,104 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
-  for (int u = lane; u < p.units; u += lanes) {
-    const int k0 = u * 128;
-    const int nsub = min(4, (p.K - k0) >> 5);
-    const bool vec16 = p.aligned16 && nsub == 4;
+  for (int t = 0; t < rounds; ++t) {
+    const int ubase = t * lanes;
+    // -- activation loads for this thread's first staged run (issued first)
+    auto run_coords = [&](int rr, int& m, int& ul, int& j) {
+      m = rr / (4 * lanes);
+      const int rem = rr - m * 4 * lanes;
+      ul = rem >> 2;
+      j = rem & 3;
+    };
+    auto run_load = [&](int rr, uint32_t (&raw)[RAW]) {
+      int m, ul, j;
+      run_coords(rr, m, ul, j);
+      const int k = (ubase + ul) * 128 + 32 * j;
+      const bool valid = rr < nruns && m < mcount && k < p.K;
+      load_raw_run<ACT>(p.x, valid ? static_cast<int64_t>(m0 + m) * p.K + k : 0, raw);
+      return valid;
+    };
+    uint32_t raw[RAW];
+    const bool raw_valid = run_load(tid, raw);
 
+    // -- weights, scales and zeros of this lane's unit (addresses clamped to
+    // the matrix; rows past N and units past K get zero scale and zero)
+    const int u = ubase + lane;
+    const bool active = u < p.units;
+    const int uc = active ? u : p.units - 1;
+    const int nsub = FAST ? 4 : min(4, (p.K - uc * 128) >> 5);
     uint32_t d[R][4 * BITS];
-    float sv[R][4], zv[R][4];
+    uint32_t sb[R][4], zb[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = n_base + r;
-      if (n < p.N) {
-        load_unit<BITS>(p.packed + static_cast<int64_t>(n) * p.row_bytes +
-                            static_cast<int64_t>(u) * 16 * BITS,
-                        vec16, nsub, d[r]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int g = min((k0 + 32 * j) / GROUP, p.groups - 1);
-          const int64_t gi = static_cast<int64_t>(n) * p.groups + g;
-          sv[r][j] = load_act<ACT>(p.scales, gi);
-          zv[r][j] = load_act<ACT>(p.zeros, gi);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4 * BITS; ++i) d[r][i] = 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { sv[r][j] = 0.0f; zv[r][j] = 0.0f; }
-      }
+      const int nc = min(n_base + r, p.N - 1);
+      load_unit<BITS, FAST>(p.packed + static_cast<int64_t>(nc) * p.row_bytes +
+                                static_cast<int64_t>(uc) * 16 * BITS, nsub, d[r]);
+      const int64_t ro = static_cast<int64_t>(nc) * p.groups;
+      load_unit_sz<ACT, GROUP, FAST>(p.scales, ro, uc, p.groups, sb[r]);
+      load_unit_sz<ACT, GROUP, FAST>(p.zeros, ro, uc, p.groups, zb[r]);
     }
 
+    // -- stage the round's activations: layout [m][j][quad][unit-in-round].
+    // The thread's first run (loaded above, before the weights) is staged
+    // outside the loop so that only the activation loads must have landed.
+    // (Threads without a run write to a scratch slot past the stage, which
+    // keeps this code unconditional so the compiler cannot sink the
+    // activation loads behind the weight loads.)
+    auto stage_store = [&](int rr, bool valid) {
+      int m, ul, j;
+      run_coords(rr, m, ul, j);
+#pragma unroll
+      for (int i = 0; i < RAW; ++i) raw[i] = valid ? raw[i] : 0u;
+      uint32_t out[QD * 4];
+      stage_run<ACT, BITS>(raw, out);
+      const bool real = rr < nruns;
+#pragma unroll
+      for (int q = 0; q < QD; ++q)
+        stage[real ? ((m * 4 + j) * QD + q) * lanes + ul : nruns * QD + q] =
+            make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+    };
+    stage_store(tid, raw_valid);
+    for (int rr = tid + blockDim.x; rr < nruns; rr += blockDim.x) {
+      const bool v = run_load(rr, raw);
+      stage_store(rr, v);
+    }
+    __syncthreads();
+
+    // -- compute (runs past K and rows past M hold zero activations, and
+    // clamped rows/units have zero scale and zero, so they add nothing)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j >= nsub) break;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (m0 + m >= p.M) break;
-        const uint8_t* xrow = static_cast<const uint8_t*>(p.x) +
-                              (static_cast<int64_t>(m0 + m) * p.K + k0 + 32 * j) * Act<ACT>::bytes;
-        uint32_t xw[XW];
-        const uint4* xs = reinterpret_cast<const uint4*>(xrow);
+        uint32_t xs[QD * 4];
 #pragma unroll
-        for (int i = 0; i < XW / 4; ++i) {
-          uint4 v = xs[i];
-          xw[4 * i + 0] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+        for (int q = 0; q < QD; ++q) {
+          const uint4 v = stage[((m * 4 + j) * QD + q) * lanes + lane];
+          xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
         }
-        float X = 0.0f;
-        if constexpr (ACT == ACT_F32) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) X += __uint_as_float(xw[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) X = dot2<ACT>(xw[i], Magic<ACT>::ones, X);
-        }
+        const float X = __uint_as_float(xs[StagedWords<ACT, BITS>::n]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          float dotq;
-          if constexpr (ACT == ACT_F32) {
-            dotq = dot_run_f32<BITS>(&d[r][j * BITS], reinterpret_cast<const float*>(xw), 0.0f);
-          } else {
-            const float P = dot_run_pairs<BITS, ACT>(&d[r][j * BITS], xw, 0.0f);
-            dotq = P - Magic<ACT>::value * X;
-          }
-          acc[r][m] = __builtin_fmaf(sv[r][j], dotq, acc[r][m]);
-          acc[r][m] = __builtin_fmaf(zv[r][j], X, acc[r][m]);
+          const float dq = run_dot<ACT, BITS>(&d[r][j * BITS], xs);
+          const bool ok = active && n_base + r < p.N;
+          const float sv = ok ? act_bits_to_float<ACT>(sb[r][j]) : 0.0f;
+          const float zv = ok ? act_bits_to_float<ACT>(zb[r][j]) : 0.0f;
+          acc[r][m] = __builtin_fmaf(sv, dq, acc[r][m]);
+          acc[r][m] = __builtin_fmaf(zv, X, acc[r][m]);
         }
       }
     }
+    if (t + 1 < rounds) __syncthreads();
   }
 
-  // combine the partial sums of the row group's lanes (stays inside the
-  // aligned group of `lanes` lanes of this wavefront)
-  for (int off = lanes >> 1; off > 0; off >>= 1) {
+  // combine the lanes of each row group with DPP; the sum lands in the
+  // group's last lane
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[r][m] += __shfl_xor(acc[r][m], off);
-  }
-  if (lane == 0) {
+    for (int m = 0; m < MT; ++m) acc[r][m] = group_sum_to_last(acc[r][m], lanes);
+  if (lane == lanes - 1) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = n_base + r;
@@ -177,21 +358,34 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
       const float b = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (m0 + m >= p.M) break;
+        if (m >= mcount) break;
         store_act<ACT>(p.y, static_cast<int64_t>(m0 + m) * p.N + n, acc[r][m] + b);
       }
     }
   }
 }
 
-template <int GROUP, int ACT>
-static hipError_t dispatch_mt(const QmvParams& p, const QmvLaunch& l, hipStream_t s) {
-  if (l.mt == 1) {
-    qmv_kernel<LOWBIT_BITS, GROUP, ACT, 1><<<l.grid, l.block, 0, s>>>(p);
+template <int GROUP, int ACT, int MT>
+static hipError_t launch_one(const QmvParams& p, const QmvLaunch& l, hipStream_t s) {
+  // staged runs plus one scratch run for threads without a run
+  const size_t lds = (static_cast<size_t>(MT) * 4 * (size_t(1) << p.lpr_shift) + 1) *
+                     RunQuads<ACT, LOWBIT_BITS>::n * 16;
+  if (p.aligned16 && p.sz_vec) {
+    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, true><<<l.grid, l.block, lds, s>>>(p);
   } else {
-    qmv_kernel<LOWBIT_BITS, GROUP, ACT, 4><<<l.grid, l.block, 0, s>>>(p);
+    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, false><<<l.grid, l.block, lds, s>>>(p);
   }
   return hipGetLastError();
+}
+
+template <int GROUP, int ACT>
+static hipError_t dispatch_mt(const QmvParams& p, const QmvLaunch& l, hipStream_t s) {
+  switch (l.mt) {
+    case 1: return launch_one<GROUP, ACT, 1>(p, l, s);
+    case 2: return launch_one<GROUP, ACT, 2>(p, l, s);
+    case 4: return launch_one<GROUP, ACT, 4>(p, l, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int GROUP>
@@ -214,6 +408,16 @@ hipError_t LOWBIT_CAT(launch_qmv_b, LOWBIT_BITS)(const QmvParams& p, const QmvLa
     case 128: return dispatch_act<128>(p, l, act, s);
     case 256: return dispatch_act<256>(p, l, act, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// Staged LDS bytes per activation row and unit of a round (host-side sizing).
+#define LOWBIT_QMV_STAGE(ACTK) (4 * RunQuads<ACTK, LOWBIT_BITS>::n * 16)
+int LOWBIT_CAT(qmv_stage_bytes_b, LOWBIT_BITS)(int act) {
+  switch (act) {
+    case ACT_F32: return LOWBIT_QMV_STAGE(ACT_F32);
+    case ACT_F16: return LOWBIT_QMV_STAGE(ACT_F16);
+    default: return LOWBIT_QMV_STAGE(ACT_BF16);
   }
 }
 
