@@ -3,7 +3,7 @@
 Every source is compiled with hipcc for --offload-arch=gfx950 with packed-fp32
 instruction selection disabled.  The quantizer is compiled with
 -ffp-contract=off so that its fp32 steps stay single operations.  The
-decode kernel is compiled once per bit width (-DLOWBIT_BITS=b).
+decode and MFMA kernels are compiled once per bit width (-DLOWBIT_BITS=b).
 """
 from __future__ import annotations
 
@@ -37,10 +37,10 @@ def hipcc() -> str:
 
 def _units():
     units = [("lowbit_api.cpp", "lowbit_api.o", []),
-             ("quant_pack.hip", "quant_pack.o", ["-ffp-contract=off"]),
-             ("qmm.hip", "qmm.o", [])]
+             ("quant_pack.hip", "quant_pack.o", ["-ffp-contract=off"])]
     for b in range(1, 8):
         units.append(("qmv.hip", f"qmv_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
+        units.append(("qmm.hip", f"qmm_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
     return units
 
 

@@ -61,16 +61,29 @@ int qmv_stage_bytes_b7(int act);
 
 // --------------------------------------------------------------------- qmm --
 struct QmmParams {
-  const void* x;
-  const uint8_t* packed;
-  const void* scales;
-  const void* zeros;
-  const void* bias;
-  void* y;
+  const void* x;          // M x K act (f16 / bf16)
+  const uint8_t* packed;  // N x row_bytes
+  const void* scales;     // N x groups act
+  const void* zeros;      // N x groups act
+  const void* bias;       // N act or nullptr
+  void* y;                // M x N act
+  float* partials;        // split-K: gridDim.z planes of M x N fp32 (workspace)
   int M, N, K;
-  int groups;
-  int64_t row_bytes;
+  int groups;             // K / group
+  int group_shift;        // log2(group)
+  int ksteps_per_split;   // 128-wide K steps per grid.z slice
+  int64_t row_bytes;      // K * bits / 8
 };
-hipError_t launch_qmm(const QmmParams& p, int bits, int group, int act, hipStream_t stream);
+struct QmmLaunch {
+  dim3 grid;              // (ceil(N/128), ceil(M/(16*mtt)), k-splits)
+  int mtt;                // 16-row MFMA tiles per block: 1, 2, 4 or 8
+};
+hipError_t launch_qmm_b1(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+hipError_t launch_qmm_b2(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+hipError_t launch_qmm_b3(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+hipError_t launch_qmm_b4(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+hipError_t launch_qmm_b5(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+hipError_t launch_qmm_b6(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+hipError_t launch_qmm_b7(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 
 }  // namespace lowbit

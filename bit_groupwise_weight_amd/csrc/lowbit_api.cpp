@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -166,18 +167,71 @@ lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, co
   return LOWBIT_OK;
 }
 
+typedef hipError_t (*QmmLauncher)(const lowbit::QmmParams&, const lowbit::QmmLaunch&, int,
+                                  hipStream_t);
+const QmmLauncher kQmm[8] = {nullptr,
+                             lowbit::launch_qmm_b1,
+                             lowbit::launch_qmm_b2,
+                             lowbit::launch_qmm_b3,
+                             lowbit::launch_qmm_b4,
+                             lowbit::launch_qmm_b5,
+                             lowbit::launch_qmm_b6,
+                             lowbit::launch_qmm_b7};
+
+// Schedule of the MFMA kernel: block tile (16*mtt) x 128, K steps of 128,
+// and a K split that brings the grid to about `target` blocks.
+struct QmmSchedule {
+  int mtt;
+  int64_t tiles_n, tiles_m, ksteps;
+  int splits, ksteps_per_split;
+  size_t partial_bytes;
+};
+
+QmmSchedule qmm_schedule(int64_t M, int64_t N, int64_t K) {
+  QmmSchedule sc{};
+  sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  sc.tiles_n = (N + 127) / 128;
+  sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
+  sc.ksteps = (K + 127) / 128;
+  const int64_t target = env_int("LOWBIT_QMM_BLOCKS", 256);
+  const int64_t tiles = sc.tiles_n * sc.tiles_m;
+  int64_t s = (target + tiles - 1) / tiles;
+  const int64_t max_split = std::max<int64_t>(1, sc.ksteps / 2);   // >= 2 steps per split
+  s = std::max<int64_t>(1, std::min<int64_t>(s, std::min<int64_t>(max_split, 64)));
+  sc.ksteps_per_split = static_cast<int>((sc.ksteps + s - 1) / s);
+  sc.splits = static_cast<int>((sc.ksteps + sc.ksteps_per_split - 1) / sc.ksteps_per_split);
+  if (sc.splits > 1) sc.partial_bytes = static_cast<size_t>(sc.splits) * M * N * sizeof(float);
+  return sc;
+}
+
 lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
                       const void* zeros, const void* bias, void* y, int bits, int group,
-                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                      int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  QmmSchedule sc = qmm_schedule(M, N, K);
+  if (sc.splits > 1 && (workspace == nullptr || workspace_bytes < sc.partial_bytes)) {
+    sc.splits = 1;                               // no workspace: one block per tile over all K
+    sc.ksteps_per_split = static_cast<int>(sc.ksteps);
+  }
+  if (sc.tiles_m > 65535 || sc.tiles_n > 0x7fffffff)
+    return fail(LOWBIT_ERR_INVALID_ARG, "problem too large for qmm");
   lowbit::QmmParams p{};
   p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
   p.M = static_cast<int>(M);
   p.N = static_cast<int>(N);
   p.K = static_cast<int>(K);
   p.groups = static_cast<int>(K / group);
+  int gs = 0;
+  while ((1 << gs) < group) ++gs;
+  p.group_shift = gs;
   p.row_bytes = K * bits / 8;
-  if ((M + 63) / 64 > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "M too large for qmm");
-  hipError_t e = lowbit::launch_qmm(p, bits, group, act_kind(act), stream);
+  p.ksteps_per_split = sc.ksteps_per_split;
+  if (sc.splits > 1) p.partials = static_cast<float*>(workspace);
+  lowbit::QmmLaunch l{};
+  l.mtt = sc.mtt;
+  l.grid = dim3(static_cast<unsigned>(sc.tiles_n), static_cast<unsigned>(sc.tiles_m),
+                static_cast<unsigned>(sc.splits));
+  hipError_t e = kQmm[bits](p, l, act_kind(act), stream);
   if (e != hipSuccess) return hip_fail(e, "qmm launch");
   return LOWBIT_OK;
 }
@@ -252,8 +306,12 @@ lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t 
 
 size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, int64_t K,
                                      lowbit_dtype act_dtype) {
-  (void)bits; (void)group; (void)M; (void)N; (void)K; (void)act_dtype;
-  return 0;
+  if (!valid_bits(bits) || !valid_group(group) || M <= 0 || N <= 0 || K <= 0 || K % group != 0 ||
+      M > kMaxDim || N > kMaxDim || K > kMaxDim || !valid_dtype(act_dtype))
+    return 0;
+  if (act_dtype == LOWBIT_F32) return 0;         // fp32 runs the decode kernel only
+  const QmmSchedule sc = qmm_schedule(M, N, K);
+  return sc.partial_bytes;
 }
 
 lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
@@ -289,7 +347,9 @@ lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const ui
   else use_qmm = (M >= kQmmMinM) && act_dtype != LOWBIT_F32;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_qmm) return run_qmm(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
+  if (use_qmm)
+    return run_qmm(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, workspace,
+                   workspace_bytes, s);
   return run_qmv(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
 }
 

@@ -1,24 +1,45 @@
 // Matrix-matrix kernel (M >= 16): y = x . dequant(Wq)^T (+ bias) on MFMA.
 //
 // The pages ask whether the decode approach of "metal lowbit kernels:
-// qmv_fast optimization" would also work for a GEMM (closing review comment);
-// batched int4 weight-only decode on the H100 table of "Add support for fbgemm
-// int4 mm kernel" shows why a batched path matters.  Here each K-step of a
-// weight tile is dequantized once (w = s*q + z in fp32, rounded to the
-// activation type) into LDS and consumed by v_mfma_f32_16x16x32_{f16,bf16}
-// with fp32 accumulation.
+// qmv_fast optimization" also works for a GEMM (closing review comment), and
+// the H100 table of "Add support for fbgemm int4 mm kernel" shows batched
+// int4 weight-only decode falling far behind -- the batched path matters.
 //
-// Tile: 64 (M) x 64 (N) per 256-thread block, K-step 32 (one MFMA deep, and
-// never more than one group since every group size is a multiple of 32).
-// Wave w computes the 32 x 32 sub-tile (w & 1, w >> 1) as 2 x 2 MFMA tiles.
+// Layout on CDNA4 (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation):
+//   * block tile: 16*MTT rows (M) x 128 columns (N); 4 waves, wave w owns
+//     columns [32w, 32w+32) as two 16-wide MFMA tiles and all M rows;
+//   * K advances in steps of 128.  Within a step, lane group g = lane/16 owns
+//     the 32 consecutive K positions [32g, 32g+32); MFMA slot 8g+t of k-sub
+//     ks (0..3) is K position 32g + 8ks + t for both operands, so each lane's
+//     weights for a step are ONE 32-code run of one row: b 32-bit words, one
+//     scale and one zero (a run never crosses a group);
+//   * weights are dequantized straight into MFMA operand registers
+//     (w = s*q + z in fp32, rounded once to the activation type) -- every
+//     column belongs to exactly one wave, so no LDS round trip is needed;
+//   * the activation tile (16*MTT x 128) is shared by the 4 waves through a
+//     double-buffered LDS stage filled by direct global->LDS loads (XOR
+//     swizzled rows, no staging registers);
+//   * the next step's codes and activations are loaded, and its weights
+//     dequantized, while the current step's MFMAs run;
+//   * split-K: blocks along grid.z own disjoint K ranges; with S > 1 each
+//     block writes an fp32 partial plane to the workspace and a second small
+//     kernel adds the planes in fixed order (results do not depend on
+//     scheduling), adds the bias and rounds once.
 #include "device_common.h"
 #include "kernels.h"
+
+#ifndef LOWBIT_BITS
+#error "compile with -DLOWBIT_BITS=<1..7>"
+#endif
 
 namespace lowbit {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162v_t __attribute__((ext_vector_type(2)));
 
 template <int ACT>
 __device__ __forceinline__ float4_t mfma16x16x32(uint4 a, uint4 b, float4_t c) {
@@ -31,132 +52,274 @@ __device__ __forceinline__ float4_t mfma16x16x32(uint4 a, uint4 b, float4_t c) {
   }
 }
 
-constexpr int QMM_BM = 64, QMM_BN = 64, QMM_BK = 32;
-constexpr int QMM_LDS_STRIDE = QMM_BK + 8;   // 16-bit elements per LDS row (pad 16 B)
+// Two fp32 values -> two activation-type values (nearest even), packed.
+template <int ACT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const float2_t v = {lo, hi};
+  if constexpr (ACT == ACT_F16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2v_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf162v_t));
+  }
+}
 
-template <int BITS, int GROUP, int ACT>
+constexpr int QMM_BN = 128;          // columns per block
+constexpr int QMM_BK = 128;          // K per step
+
+// Dequantize codes I and I+1 of a 32-code run into one packed pair.
+template <int BITS, int ACT, int I>
+__device__ __forceinline__ uint32_t dequant2(const uint32_t* w, float s, float z) {
+  const float a = __builtin_fmaf(s, static_cast<float>(code_at<BITS, I>(w)), z);
+  const float b = __builtin_fmaf(s, static_cast<float>(code_at<BITS, I + 1>(w)), z);
+  return pack2<ACT>(a, b);
+}
+
+// Dequantize the 8 codes [8ks, 8ks+8) of a 32-code run into one operand.
+template <int BITS, int ACT, int KS>
+__device__ __forceinline__ uint4 dequant8(const uint32_t* w, float s, float z) {
+  return make_uint4(dequant2<BITS, ACT, 8 * KS + 0>(w, s, z), dequant2<BITS, ACT, 8 * KS + 2>(w, s, z),
+                    dequant2<BITS, ACT, 8 * KS + 4>(w, s, z), dequant2<BITS, ACT, 8 * KS + 6>(w, s, z));
+}
+
+template <int BITS, int ACT>
+__device__ __forceinline__ void dequant_run(const uint32_t* w, float s, float z, uint4 (&b)[4]) {
+  b[0] = dequant8<BITS, ACT, 0>(w, s, z);
+  b[1] = dequant8<BITS, ACT, 1>(w, s, z);
+  b[2] = dequant8<BITS, ACT, 2>(w, s, z);
+  b[3] = dequant8<BITS, ACT, 3>(w, s, z);
+}
+
+template <int BITS, int ACT, int MTT>
 __global__ __launch_bounds__(256) void qmm_kernel(QmmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[QMM_BM * QMM_LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[QMM_BN * QMM_LDS_STRIDE];
+  constexpr int MROWS = 16 * MTT;
+  constexpr int XCH = MTT;   // 16-byte activation chunks staged per thread per step
+  // two activation stages as separate arrays, so that the compiler can tell
+  // the stage being read from the one being filled
+  __shared__ uint4 stage0[MTT * 16 * 16];
+  __shared__ uint4 stage1[MTT * 16 * 16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int m_base = blockIdx.y * QMM_BM;
-  const int n_base = blockIdx.x * QMM_BN;
-  const int wm = (wave & 1) * 32;
-  const int wn = (wave >> 1) * 32;
+  const int fr = lane & 15;           // row / column inside a 16-wide MFMA tile
+  const int g = lane >> 4;            // lane group: K positions [32g, 32g+32)
+  const int n0 = blockIdx.x * QMM_BN;
+  const int m0 = blockIdx.y * MROWS;
+  const int ksteps = (p.K + QMM_BK - 1) / QMM_BK;
+  const int s_begin = blockIdx.z * p.ksteps_per_split;
+  const int s_end = min(ksteps, s_begin + p.ksteps_per_split);
 
-  // staging roles: thread -> (row, 8-element chunk) of the 64 x 32 tiles
-  const int st_row = tid >> 2;
-  const int st_chunk = tid & 3;
-  const int am = m_base + st_row;
-  const int bn = n_base + st_row;
-
-  float4_t acc[2][2];
+  // ---- weight rows of this lane (clamped; out-of-range columns get s=z=0)
+  int ncol[2];
+  bool nok[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < p.K; k0 += QMM_BK) {
-    // ---- activations: 8 elements (16 B) per thread
-    uint4 av = make_uint4(0, 0, 0, 0);
-    if (am < p.M) {
-      av = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) +
-                                           static_cast<int64_t>(am) * p.K + k0 + 8 * st_chunk);
-    }
-    // ---- weights: 8 codes = BITS bytes per thread, dequantized to 16-bit
-    uint4 bv = make_uint4(0, 0, 0, 0);
-    if (bn < p.N) {
-      const uint8_t* src = p.packed + static_cast<int64_t>(bn) * p.row_bytes +
-                           ((k0 + 8 * st_chunk) >> 3) * BITS;
-      uint64_t stream = 0;
-#pragma unroll
-      for (int b = 0; b < BITS; ++b) stream |= static_cast<uint64_t>(src[b]) << (8 * b);
-      const int64_t gi = static_cast<int64_t>(bn) * p.groups + k0 / GROUP;
-      const float s = load_act<ACT>(p.scales, gi);
-      const float z = load_act<ACT>(p.zeros, gi);
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float q = static_cast<float>((stream >> (i * BITS)) & ((1u << BITS) - 1u));
-        h[i] = float_to_act_bits<ACT>(__builtin_fmaf(s, q, z));
-      }
-      bv = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                      h[6] | (h[7] << 16));
-    }
-    *reinterpret_cast<uint4*>(&As[st_row * QMM_LDS_STRIDE + 8 * st_chunk]) = av;
-    *reinterpret_cast<uint4*>(&Bs[st_row * QMM_LDS_STRIDE + 8 * st_chunk]) = bv;
-    __syncthreads();
-
-    const int fr = lane & 15;        // row within a 16-row MFMA tile
-    const int fk = (lane >> 4) * 8;  // first K of this lane's 8 elements
-    uint4 a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(&As[(wm + 16 * i + fr) * QMM_LDS_STRIDE + fk]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(&Bs[(wn + 16 * j + fr) * QMM_LDS_STRIDE + fk]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32<ACT>(a[i], b[j], acc[i][j]);
-    __syncthreads();
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = n0 + 32 * wave + 16 * nt + fr;
+    nok[nt] = n < p.N;
+    ncol[nt] = nok[nt] ? n : p.N - 1;
   }
 
-  // ---- epilogue: lane holds D[4*(lane/16) + r][lane % 16] of each 16x16 tile
+  auto load_codes = [&](int step, uint32_t (&w)[2][BITS], uint32_t (&sb)[2], uint32_t (&zb)[2],
+                        bool& kok) {
+    const int k = step * QMM_BK + 32 * g;
+    kok = k < p.K;
+    const int kc = kok ? k : p.K - 32;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n_base + wn + 16 * j + (lane & 15);
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          p.packed + static_cast<int64_t>(ncol[nt]) * p.row_bytes + (kc >> 3) * BITS);
+#pragma unroll
+      for (int i = 0; i < BITS; ++i) w[nt][i] = src[i];
+      const int64_t gi = static_cast<int64_t>(ncol[nt]) * p.groups + (kc >> p.group_shift);
+      sb[nt] = static_cast<const typename Act<ACT>::bits_t*>(p.scales)[gi];
+      zb[nt] = static_cast<const typename Act<ACT>::bits_t*>(p.zeros)[gi];
+    }
+  };
+  auto dequant = [&](const uint32_t (&w)[2][BITS], const uint32_t (&sb)[2],
+                     const uint32_t (&zb)[2], bool kok, uint4 (&b)[2][4]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bool ok = kok && nok[nt];
+      const float s = ok ? act_bits_to_float<ACT>(sb[nt]) : 0.0f;
+      const float z = ok ? act_bits_to_float<ACT>(zb[nt]) : 0.0f;
+      dequant_run<BITS, ACT>(w[nt], s, z, b[nt]);
+    }
+  };
+  // Activation stage: the 16*MTT x 128 tile of one step, rows of 256 bytes
+  // (16 chunks of 8 elements) with chunk c of row r stored at position
+  // c ^ (r & 15) -- the 16 lanes that read one k-sub of an MFMA tile then hit
+  // 16 different 16-byte bank groups.  It is filled with direct global->LDS
+  // loads (lane i of a wave lands at dst + 16 i), so it costs no registers:
+  // wave w's load i covers rows 4*(4i + w) .. +3, and each lane fetches the
+  // chunk that belongs at its position.  Rows past M and chunks past K read a
+  // clamped in-range address: a row past M only feeds output rows that are
+  // never stored, and past K the weights are dequantized with s = z = 0.
+  auto load_x_lds = [&](int step, uint4* stage) {
+    uint8_t* base = reinterpret_cast<uint8_t*>(stage);
+#pragma unroll
+    for (int i = 0; i < MTT; ++i) {
+      const int r0 = 4 * (4 * i + wave);
+      const int row = r0 + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      const int grow = min(m0 + row, p.M - 1);
+      const int k = min(step * QMM_BK + 8 * c, p.K - 8);
+      const uint16_t* src = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(grow) * p.K + k;
+      __builtin_amdgcn_global_load_lds(src, base + r0 * 256, 16, 0, 0);
+    }
+  };
+
+  float4_t acc[MTT][2];
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (s_begin < s_end) {
+    // Pipeline: codes are fetched two steps ahead (register sets A and B
+    // alternate), activations one step ahead (LDS stages 0 and 1 alternate),
+    // and the next step's weights are dequantized (operand sets b0 / b1
+    // alternate) while this step's MFMAs run.  Steps past the block's range
+    // re-read the last step (clamped) and are never used.
+    uint32_t wa[2][BITS], sa[2], za[2], wb[2][BITS], sbb[2], zbb[2];
+    bool ka, kb;
+    uint4 b0[2][4], b1[2][4];
+    const int last = s_end - 1;
+    load_codes(s_begin, wa, sa, za, ka);
+    load_x_lds(s_begin, stage0);
+    load_codes(min(s_begin + 1, last), wb, sbb, zbb, kb);
+    dequant(wa, sa, za, ka, b0);
+    __builtin_amdgcn_s_waitcnt(0);    // stage 0 has landed in LDS
+    __syncthreads();
+
+    // one K step: multiply `read` x `bc`; prefetch codes of step+2 into the
+    // set that just became free, activations of step+1 into `fill`, and
+    // dequantize step+1 (codes in `wn`) into `bn`
+    auto run_step = [&](int step, const uint4* read, uint4* fill, const uint4 (&bc)[2][4],
+                        uint4 (&bn)[2][4], uint32_t (&wn)[2][BITS], uint32_t (&sn)[2],
+                        uint32_t (&zn)[2], bool& kn, uint32_t (&wf)[2][BITS], uint32_t (&sf)[2],
+                        uint32_t (&zf)[2], bool& kf) {
+      const bool more = step + 1 < s_end;
+      load_codes(min(step + 2, last), wf, sf, zf, kf);
+      if (more) load_x_lds(step + 1, fill);
+      const uint8_t* abase = reinterpret_cast<const uint8_t*>(read);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < MTT; ++mt) {
+          const uint4 a = *reinterpret_cast<const uint4*>(
+              abase + (16 * mt + fr) * 256 + (((4 * g + ks) ^ fr) << 4));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32<ACT>(a, bc[nt][ks], acc[mt][nt]);
+        }
+      }
+      dequant(wn, sn, zn, kn, bn);
+      __builtin_amdgcn_s_waitcnt(0);  // next stage landed; this one fully read
+      __syncthreads();
+    };
+    for (int step = s_begin; step < s_end; step += 2) {
+      // codes: step+1 in B, step+2 -> A
+      run_step(step, stage0, stage1, b0, b1, wb, sbb, zbb, kb, wa, sa, za, ka);
+      if (step + 1 < s_end)   // codes: step+2 in A, step+3 -> B
+        run_step(step + 1, stage1, stage0, b1, b0, wa, sa, za, ka, wb, sbb, zbb, kb);
+    }
+  }
+
+  // ---- epilogue.  Lane holds D[4*g + r][fr] of each 16x16 tile.
+  if (gridDim.z == 1) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = n0 + 32 * wave + 16 * nt + fr;
+      if (n >= p.N) continue;
+      const float bias = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 16 * mt + 4 * g + r;
+          if (m < p.M) store_act<ACT>(p.y, static_cast<int64_t>(m) * p.N + n, acc[mt][nt][r] + bias);
+        }
+    }
+    return;
+  }
+
+  // split-K: this block's fp32 partial sums go to plane blockIdx.z of the
+  // workspace; qmm_reduce adds the planes in order.
+  float* part = p.partials + static_cast<int64_t>(blockIdx.z) * p.M * p.N;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = n0 + 32 * wave + 16 * nt + fr;
     if (n >= p.N) continue;
-    const float bias = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int mt = 0; mt < MTT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m_base + wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < p.M) store_act<ACT>(p.y, static_cast<int64_t>(m) * p.N + n, acc[i][j][r] + bias);
+        const int m = m0 + 16 * mt + 4 * g + r;
+        if (m < p.M) part[static_cast<int64_t>(m) * p.N + n] = acc[mt][nt][r];
       }
-    }
   }
 }
 
-template <int BITS, int GROUP>
-static hipError_t dispatch_act(const QmmParams& p, int act, dim3 g, dim3 b, hipStream_t s) {
-  switch (act) {
-    case ACT_F16: qmm_kernel<BITS, GROUP, ACT_F16><<<g, b, 0, s>>>(p); break;
-    case ACT_BF16: qmm_kernel<BITS, GROUP, ACT_BF16><<<g, b, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
+// y = sum over the split planes (in plane order) + bias, rounded once.
+// Each thread produces 4 consecutive outputs of one row.
+template <int ACT>
+__global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, int splits) {
+  const int64_t quads_per_row = (p.N + 3) / 4;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= quads_per_row * p.M) return;
+  const int m = static_cast<int>(q / quads_per_row);
+  const int n = static_cast<int>(q - static_cast<int64_t>(m) * quads_per_row) * 4;
+  const int64_t plane = static_cast<int64_t>(p.M) * p.N;
+  const int64_t idx = static_cast<int64_t>(m) * p.N + n;
+  const int cnt = min(4, p.N - n);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (cnt == 4 && (p.N % 4) == 0) {
+    for (int z = 0; z < splits; ++z) {
+      const float4 t = *reinterpret_cast<const float4*>(p.partials + z * plane + idx);
+      v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+    }
+  } else {
+    for (int z = 0; z < splits; ++z)
+      for (int i = 0; i < cnt; ++i) v[i] += p.partials[z * plane + idx + i];
   }
+  for (int i = 0; i < cnt; ++i) {
+    const float b = p.bias ? load_act<ACT>(p.bias, n + i) : 0.0f;
+    store_act<ACT>(p.y, idx + i, v[i] + b);
+  }
+}
+
+template <int ACT, int MTT>
+static hipError_t launch_mtt(const QmmParams& p, dim3 grid, hipStream_t s) {
+  qmm_kernel<LOWBIT_BITS, ACT, MTT><<<grid, dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <int BITS>
-static hipError_t dispatch_group(const QmmParams& p, int group, int act, dim3 g, dim3 b,
-                                 hipStream_t s) {
-  switch (group) {
-    case 32: return dispatch_act<BITS, 32>(p, act, g, b, s);
-    case 64: return dispatch_act<BITS, 64>(p, act, g, b, s);
-    case 128: return dispatch_act<BITS, 128>(p, act, g, b, s);
-    case 256: return dispatch_act<BITS, 256>(p, act, g, b, s);
+template <int ACT>
+static hipError_t launch_act(const QmmParams& p, int mtt, dim3 grid, hipStream_t s) {
+  switch (mtt) {
+    case 1: return launch_mtt<ACT, 1>(p, grid, s);
+    case 2: return launch_mtt<ACT, 2>(p, grid, s);
+    case 4: return launch_mtt<ACT, 4>(p, grid, s);
+    case 8: return launch_mtt<ACT, 8>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_qmm(const QmmParams& p, int bits, int group, int act, hipStream_t s) {
-  dim3 grid((p.N + QMM_BN - 1) / QMM_BN, (p.M + QMM_BM - 1) / QMM_BM), block(256);
-  switch (bits) {
-    case 1: return dispatch_group<1>(p, group, act, grid, block, s);
-    case 2: return dispatch_group<2>(p, group, act, grid, block, s);
-    case 3: return dispatch_group<3>(p, group, act, grid, block, s);
-    case 4: return dispatch_group<4>(p, group, act, grid, block, s);
-    case 5: return dispatch_group<5>(p, group, act, grid, block, s);
-    case 6: return dispatch_group<6>(p, group, act, grid, block, s);
-    case 7: return dispatch_group<7>(p, group, act, grid, block, s);
+#define LOWBIT_CAT2(a, b) a##b
+#define LOWBIT_CAT(a, b) LOWBIT_CAT2(a, b)
+hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLaunch& l, int act,
+                                                 hipStream_t s) {
+  hipError_t e;
+  switch (act) {
+    case ACT_F16: e = launch_act<ACT_F16>(p, l.mtt, l.grid, s); break;
+    case ACT_BF16: e = launch_act<ACT_BF16>(p, l.mtt, l.grid, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || l.grid.z == 1) return e;
+  const int64_t quads = static_cast<int64_t>(p.M) * ((p.N + 3) / 4);
+  const dim3 rgrid(static_cast<unsigned>((quads + 255) / 256));
+  if (act == ACT_F16) qmm_reduce_kernel<ACT_F16><<<rgrid, dim3(256), 0, s>>>(p, l.grid.z);
+  else qmm_reduce_kernel<ACT_BF16><<<rgrid, dim3(256), 0, s>>>(p, l.grid.z);
+  return hipGetLastError();
 }
 
 }  // namespace lowbit

@@ -170,11 +170,33 @@ def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch
     return packed, scales, zeros, codes
 
 
+# Workspaces kept per (device, stream): calls on one stream run in order, so
+# they never use the same workspace at the same time.
+_workspaces = {}
+
+
+def cached_workspace(device: torch.device, stream_handle, nbytes: int) -> Optional[torch.Tensor]:
+    """A device buffer of at least nbytes reserved for calls on this stream."""
+    if nbytes <= 0:
+        return None
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                   bias: Optional[torch.Tensor], bits: int, group: int,
                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   path: Optional[int] = None, stream=None) -> torch.Tensor:
-    """y[M, N] = x[M, K] . dequant(packed, scales, zeros)^T (+ bias), on the GPU."""
+    """y[M, N] = x[M, K] . dequant(packed, scales, zeros)^T (+ bias), on the GPU.
+
+    Without an explicit `workspace`, a buffer cached for this device and
+    stream is used (calls on one stream run in order, so they never share it
+    concurrently).
+    """
     lib = load()
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
@@ -182,11 +204,14 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
     N = scales.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    s = _stream_handle(x.device, stream)
+    if workspace is None and M > 0 and x.dtype in _DTYPE_ENUM:
+        need = lib.lowbit_linear_workspace_bytes(bits, group, M, N, K, _DTYPE_ENUM[x.dtype])
+        workspace = cached_workspace(x.device, s, need)
     _require_cuda(x, packed, scales, zeros, bias, y, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _DTYPE_ENUM[x.dtype], _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(bias),
             _ptr(y), bits, group, M, N, K, _ptr(workspace), ws_bytes)
-    s = _stream_handle(x.device, stream)
     if path is None:
         st = lib.lowbit_linear(*args, s)
         _check(st, "lowbit_linear")

@@ -129,10 +129,11 @@ size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, 
  *   M >= 0 (M == 0 is a no-op that returns LOWBIT_OK; x and y may then be
  *   NULL), N > 0, K > 0,
  *   K % group == 0.
- *   workspace/workspace_bytes: device scratch or NULL/0.  When non-NULL it
- *            must be 256-byte aligned and zero-filled before its first use;
- *            every call leaves it zero-filled again.  Calls that run
- *            concurrently must not share one workspace.
+ *   workspace/workspace_bytes: device scratch or NULL/0 (see
+ *            lowbit_linear_workspace_bytes).  When non-NULL it must be
+ *            256-byte aligned; its contents on entry do not matter and are
+ *            overwritten.  Calls that run concurrently must not share one
+ *            workspace.
  *
  * Products accumulate in fp32; the bias is added in fp32 and the result is
  * rounded to act_dtype to nearest even.  Identical inputs give bitwise
