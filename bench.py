@@ -34,6 +34,27 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 ROTATE_BYTES = 1 << 30
 
+# HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes whose
+# commands and scaling are recorded in profiles/ (FETCH_SIZE x 1.9997,
+# WRITE_SIZE x 1.0000, from a plain 256 MiB copy).  They describe the
+# kernel sources whose sha256 prefix is `src_hash`; for any other sources bench
+# reports traffic as null.
+MEASURED_TRAFFIC = {
+    "src_hash": "5e0c99487a5a2132",
+    "qmv_bits1to7_bytes": 67398148,
+    "qmm_bytes": {"4096x14336": 92089237, "14336x4096": 95508337},
+}
+
+
+def kernel_source_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_groupwise_weight_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -48,6 +69,9 @@ def parse():
                     help="launches per kernel in the per-kernel timing loops")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-reps", type=int, default=30)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (a kernel of known "
+                         "traffic, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -176,6 +200,14 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 268435456 bytes read + 268435456 bytes written")
+
     qcases, mcases = qmv_cases(), qmm_cases()
     qmv_bytes_all = sum(algo_bytes(c) for c in qcases)
     qmm_bytes_all = sum(algo_bytes(c) for c in mcases)
@@ -241,6 +273,9 @@ def main():
         qmm.append({"K": c.K, "N": c.N, "M": c.M, "us": round(us, 3), "TFLOP_s": round(tf, 2),
                     "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
         log(f"qmm K={c.K} N={c.N}: {us:.3f} us  {tf:.2f} TFLOP/s")
+    fresh = kernel_source_hash() == MEASURED_TRAFFIC["src_hash"]
+    qmv_traffic = MEASURED_TRAFFIC["qmv_bits1to7_bytes"] if fresh else None
+    qmm_traffic = (sum(MEASURED_TRAFFIC["qmm_bytes"].values()) if fresh else None)
     qmm_fl = sum(2.0 * c.M * c.N * c.K for c in mcases)
     qmm_tf = qmm_fl / (sum(qmm_us) * 1e-6) / 1e12
 
@@ -269,7 +304,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(qmv_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": qmv_traffic,
+            "traffic_note": "HBM bytes of one pass over the 7 launches (rocprofv3 FETCH_SIZE + "
+                            "WRITE_SIZE, scaled); algorithmic bytes of that pass: "
+                            + str(qmv_bytes_all),
         },
         "qmv_by_bits": per_bit,
         "qmv_total_us": round(qmv_total_us, 3),
@@ -280,7 +318,9 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(qmm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": qmm_traffic,
+            "traffic_note": "HBM bytes of the two shapes' launches incl. the split-K reduce "
+                            "(rocprofv3, scaled); algorithmic bytes: " + str(qmm_bytes_all),
         },
         "qmm": qmm,
         "qmv_eager_us_per_call": [round(u, 3) for u in eager_us],
