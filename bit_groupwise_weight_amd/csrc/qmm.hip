@@ -81,6 +81,12 @@ __device__ __forceinline__ uint4 dequant8(const uint32_t* w, float s, float z) {
                     dequant2<BITS, ACT, 8 * KS + 4>(w, s, z), dequant2<BITS, ACT, 8 * KS + 6>(w, s, z));
 }
 
+// Dequantize k-sub KS (codes [8KS, 8KS+8)) of a 32-code run.
+template <int BITS, int ACT, int KS>
+__device__ __forceinline__ uint4 dequant_ks(const uint32_t* w, float s, float z) {
+  return dequant8<BITS, ACT, KS>(w, s, z);
+}
+
 template <int BITS, int ACT>
 __device__ __forceinline__ void dequant_run(const uint32_t* w, float s, float z, uint4 (&b)[4]) {
   b[0] = dequant8<BITS, ACT, 0>(w, s, z);
@@ -89,8 +95,9 @@ __device__ __forceinline__ void dequant_run(const uint32_t* w, float s, float z,
   b[3] = dequant8<BITS, ACT, 3>(w, s, z);
 }
 
+// Two waves per SIMD (two blocks per CU): the register budget is 256 per wave.
 template <int BITS, int ACT, int MTT>
-__global__ __launch_bounds__(256) void qmm_kernel(QmmParams p) {
+__global__ __launch_bounds__(256, 2) void qmm_kernel(QmmParams p) {
   constexpr int MROWS = 16 * MTT;
   constexpr int XCH = MTT;   // 16-byte activation chunks staged per thread per step
   // two activation stages as separate arrays, so that the compiler can tell
@@ -174,54 +181,90 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmParams p) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  // activation operands of k-sub ks (16 rows per MFMA tile, 8 K each)
+  auto read_a = [&](const uint8_t* abase, int ks, uint4 (&a)[MTT]) {
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+      a[mt] = *reinterpret_cast<const uint4*>(abase + (16 * mt + fr) * 256 +
+                                              (((4 * g + ks) ^ fr) << 4));
+  };
+  auto mma = [&](const uint4 (&bc)[2][4], int ks, const uint4 (&a)[MTT]) {
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32<ACT>(a[mt], bc[nt][ks], acc[mt][nt]);
+  };
+
   if (s_begin < s_end) {
     // Pipeline: codes are fetched two steps ahead (register sets A and B
-    // alternate), activations one step ahead (LDS stages 0 and 1 alternate),
-    // and the next step's weights are dequantized (operand sets b0 / b1
-    // alternate) while this step's MFMAs run.  Steps past the block's range
-    // re-read the last step (clamped) and are never used.
+    // alternate), activations one step ahead (LDS stages 0 and 1 alternate).
+    // The weight operands live in one register set: right after the MFMAs of
+    // k-sub ks are issued, k-sub ks of the next step is dequantized into the
+    // same registers, so dequantization overlaps the remaining MFMAs.  The
+    // loop always runs an even number of steps: a step past the block's
+    // range loads clamped, in-range addresses and multiplies by weights
+    // dequantized with s = z = 0, so it adds nothing -- keeping the loop body
+    // free of branches lets the accumulators stay in place.
     uint32_t wa[2][BITS], sa[2], za[2], wb[2][BITS], sbb[2], zbb[2];
     bool ka, kb;
-    uint4 b0[2][4], b1[2][4];
-    const int last = s_end - 1;
-    load_codes(s_begin, wa, sa, za, ka);
+    uint4 bop[2][4];
+    auto load_step = [&](int step, uint32_t (&w)[2][BITS], uint32_t (&sb)[2], uint32_t (&zb)[2],
+                         bool& kok) {
+      load_codes(min(step, s_end - 1), w, sb, zb, kok);
+      kok = kok && step < s_end;
+    };
+    auto scale_zero = [&](const uint32_t (&sb)[2], const uint32_t (&zb)[2], bool kok, float (&sv)[2],
+                          float (&zv)[2]) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const bool ok = kok && nok[nt];
+        sv[nt] = ok ? act_bits_to_float<ACT>(sb[nt]) : 0.0f;
+        zv[nt] = ok ? act_bits_to_float<ACT>(zb[nt]) : 0.0f;
+      }
+    };
+    load_step(s_begin, wa, sa, za, ka);
     load_x_lds(s_begin, stage0);
-    load_codes(min(s_begin + 1, last), wb, sbb, zbb, kb);
-    dequant(wa, sa, za, ka, b0);
+    load_step(s_begin + 1, wb, sbb, zbb, kb);
+    dequant(wa, sa, za, ka, bop);
     __builtin_amdgcn_s_waitcnt(0);    // stage 0 has landed in LDS
     __syncthreads();
 
-    // one K step: multiply `read` x `bc`; prefetch codes of step+2 into the
-    // set that just became free, activations of step+1 into `fill`, and
-    // dequantize step+1 (codes in `wn`) into `bn`
-    auto run_step = [&](int step, const uint4* read, uint4* fill, const uint4 (&bc)[2][4],
-                        uint4 (&bn)[2][4], uint32_t (&wn)[2][BITS], uint32_t (&sn)[2],
-                        uint32_t (&zn)[2], bool& kn, uint32_t (&wf)[2][BITS], uint32_t (&sf)[2],
-                        uint32_t (&zf)[2], bool& kf) {
-      const bool more = step + 1 < s_end;
-      load_codes(min(step + 2, last), wf, sf, zf, kf);
-      if (more) load_x_lds(step + 1, fill);
-      const uint8_t* abase = reinterpret_cast<const uint8_t*>(read);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < MTT; ++mt) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              abase + (16 * mt + fr) * 256 + (((4 * g + ks) ^ fr) << 4));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32<ACT>(a, bc[nt][ks], acc[mt][nt]);
-        }
-      }
-      dequant(wn, sn, zn, kn, bn);
-      __builtin_amdgcn_s_waitcnt(0);  // next stage landed; this one fully read
-      __syncthreads();
-    };
-    for (int step = s_begin; step < s_end; step += 2) {
-      // codes: step+1 in B, step+2 -> A
-      run_step(step, stage0, stage1, b0, b1, wb, sbb, zbb, kb, wa, sa, za, ka);
-      if (step + 1 < s_end)   // codes: step+2 in A, step+3 -> B
-        run_step(step + 1, stage1, stage0, b1, b0, wa, sa, za, ka, wb, sbb, zbb, kb);
+    // One K step: multiply `read` x bop; fetch the codes of step+2 into the
+    // register set that just became free and the activations of step+1 into
+    // `fill`; dequantize step+1 (codes already in `wn`) into bop, k-sub by
+    // k-sub, behind the MFMAs that last read it.
+#define LOWBIT_QMM_DQ(KS, WN, SV, ZV)                                                         \
+    bop[0][KS] = dequant_ks<BITS, ACT, KS>(WN[0], SV[0], ZV[0]);                              \
+    bop[1][KS] = dequant_ks<BITS, ACT, KS>(WN[1], SV[1], ZV[1]);
+#define LOWBIT_QMM_STEP(STEP, READ, FILL, WN, SN, ZN, KN, WF, SF, ZF, KF)                     \
+    {                                                                                        \
+      load_step((STEP) + 2, WF, SF, ZF, KF);                                                 \
+      load_x_lds(min((STEP) + 1, s_end - 1), FILL);                                          \
+      const uint8_t* abase = reinterpret_cast<const uint8_t*>(READ);                         \
+      float sv[2], zv[2];                                                                    \
+      scale_zero(SN, ZN, KN, sv, zv);                                                        \
+      uint4 a0[MTT], a1[MTT];                                                                \
+      read_a(abase, 0, a0);                                                                  \
+      read_a(abase, 1, a1);                                                                  \
+      mma(bop, 0, a0);                                                                       \
+      LOWBIT_QMM_DQ(0, WN, sv, zv)                                                           \
+      read_a(abase, 2, a0);                                                                  \
+      mma(bop, 1, a1);                                                                       \
+      LOWBIT_QMM_DQ(1, WN, sv, zv)                                                           \
+      read_a(abase, 3, a1);                                                                  \
+      mma(bop, 2, a0);                                                                       \
+      LOWBIT_QMM_DQ(2, WN, sv, zv)                                                           \
+      mma(bop, 3, a1);                                                                       \
+      LOWBIT_QMM_DQ(3, WN, sv, zv)                                                           \
+      __builtin_amdgcn_s_waitcnt(0); /* next stage landed; this one fully read */            \
+      __syncthreads();                                                                       \
     }
+    for (int step = s_begin; step < s_end; step += 2) {
+      LOWBIT_QMM_STEP(step, stage0, stage1, wb, sbb, zbb, kb, wa, sa, za, ka)
+      LOWBIT_QMM_STEP(step + 1, stage1, stage0, wa, sa, za, ka, wb, sbb, zbb, kb)
+    }
+#undef LOWBIT_QMM_STEP
+#undef LOWBIT_QMM_DQ
   }
 
   // ---- epilogue.  Lane holds D[4*g + r][fr] of each 16x16 tile.
@@ -273,7 +316,16 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, int splits
   const int cnt = min(4, p.N - n);
   float v[4] = {0.f, 0.f, 0.f, 0.f};
   if (cnt == 4 && (p.N % 4) == 0) {
-    for (int z = 0; z < splits; ++z) {
+    // planes are read four at a time so that their loads are in flight together
+    int z = 0;
+    for (; z + 4 <= splits; z += 4) {
+      float4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const float4*>(p.partials + (z + u) * plane + idx);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { v[0] += t[u].x; v[1] += t[u].y; v[2] += t[u].z; v[3] += t[u].w; }
+    }
+    for (; z < splits; ++z) {
       const float4 t = *reinterpret_cast<const float4*>(p.partials + z * plane + idx);
       v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
     }
