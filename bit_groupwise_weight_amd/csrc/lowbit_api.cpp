@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -119,6 +120,20 @@ int env_int(const char* name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
                       const void* zeros, const void* bias, void* y, int bits, int group,
                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -146,7 +161,7 @@ lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, co
   if (per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
   const int R = (l.mt == 1) ? 2 : 1;
 
-  // Block size: 256 threads unless that leaves fewer than ~2 blocks per CU.
+  // Block size: 256 threads unless that leaves fewer blocks than CUs.
   int threads = env_int("LOWBIT_QMV_BLOCK", 0);
   auto blocks_for = [&](int t) {
     const int64_t rows_per_block = static_cast<int64_t>(t >> shift) * R;
@@ -154,7 +169,7 @@ lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, co
   };
   if (threads != 64 && threads != 128 && threads != 256) {
     threads = 256;
-    while (threads > 128 && blocks_for(threads) < 512 && (threads >> 1) >= lanes) threads >>= 1;
+    while (threads > 64 && blocks_for(threads) < device_cus() && (threads >> 1) >= lanes) threads >>= 1;
   }
   if (threads < lanes) threads = lanes;
   const int64_t bx = blocks_for(threads);
@@ -181,7 +196,7 @@ const QmmLauncher kQmm[8] = {nullptr,
 // Schedule of the MFMA kernel: block tile (16*mtt) x 128, K steps of 128,
 // and a K split that brings the grid to about `target` blocks.
 struct QmmSchedule {
-  int mtt;
+  int mtt, nt;
   int64_t tiles_n, tiles_m, ksteps;
   int splits, ksteps_per_split;
   size_t partial_bytes;
@@ -190,12 +205,16 @@ struct QmmSchedule {
 QmmSchedule qmm_schedule(int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  sc.tiles_n = (N + 127) / 128;
+  sc.nt = env_int("LOWBIT_QMM_NT", 2) == 4 ? 4 : 2;
+  sc.tiles_n = (N + 64 * sc.nt - 1) / (64 * sc.nt);
   sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
   sc.ksteps = (K + 127) / 128;
-  const int64_t target = env_int("LOWBIT_QMM_BLOCKS", 256);
+  // One block per CU (each block takes a whole CU's register file): split K
+  // just enough that the tiles times the splits fill the CUs without a
+  // second, partial wave of blocks.
+  const int64_t target = env_int("LOWBIT_QMM_BLOCKS", device_cus());
   const int64_t tiles = sc.tiles_n * sc.tiles_m;
-  int64_t s = (target + tiles - 1) / tiles;
+  int64_t s = std::max<int64_t>(1, target / tiles);
   const int64_t max_split = std::max<int64_t>(1, sc.ksteps / 2);   // >= 2 steps per split
   s = std::max<int64_t>(1, std::min<int64_t>(s, std::min<int64_t>(max_split, 64)));
   sc.ksteps_per_split = static_cast<int>((sc.ksteps + s - 1) / s);
@@ -229,6 +248,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   if (sc.splits > 1) p.partials = static_cast<float*>(workspace);
   lowbit::QmmLaunch l{};
   l.mtt = sc.mtt;
+  l.nt = sc.nt;
   l.grid = dim3(static_cast<unsigned>(sc.tiles_n), static_cast<unsigned>(sc.tiles_m),
                 static_cast<unsigned>(sc.splits));
   hipError_t e = kQmm[bits](p, l, act_kind(act), stream);

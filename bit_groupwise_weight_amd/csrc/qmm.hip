@@ -6,25 +6,31 @@
 // int4 weight-only decode falling far behind -- the batched path matters.
 //
 // Layout on CDNA4 (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation):
-//   * block tile: 16*MTT rows (M) x 128 columns (N); 4 waves, wave w owns
-//     columns [32w, 32w+32) as two 16-wide MFMA tiles and all M rows;
+//   * block tile: 16*MTT rows (M) x 64*NT columns (N); 4 waves, wave w owns
+//     NT 16-wide column tiles and all M rows; one block per CU;
 //   * K advances in steps of 128.  Within a step, lane group g = lane/16 owns
 //     the 32 consecutive K positions [32g, 32g+32); MFMA slot 8g+t of k-sub
 //     ks (0..3) is K position 32g + 8ks + t for both operands, so each lane's
-//     weights for a step are ONE 32-code run of one row: b 32-bit words, one
-//     scale and one zero (a run never crosses a group);
+//     weights for a step are ONE 32-code run per column tile: b 32-bit
+//     words, one scale and one zero (a run never crosses a group);
 //   * weights are dequantized straight into MFMA operand registers
 //     (w = s*q + z in fp32, rounded once to the activation type) -- every
 //     column belongs to exactly one wave, so no LDS round trip is needed;
-//   * the activation tile (16*MTT x 128) is shared by the 4 waves through a
-//     double-buffered LDS stage filled by direct global->LDS loads (XOR
-//     swizzled rows, no staging registers);
-//   * the next step's codes and activations are loaded, and its weights
-//     dequantized, while the current step's MFMAs run;
+//     4-bit codes are split into even / odd byte planes so that each code
+//     converts straight from a byte;
+//   * the activation tile (16*MTT x 128) is shared by the 4 waves through
+//     two LDS stages (XOR-swizzled rows); it is loaded into registers two
+//     steps ahead and stored into the next stage while the current one is
+//     read;
+//   * codes are loaded two steps ahead; the MFMAs of each k-sub are issued
+//     in a fixed order with the dequantization of the next k-sub spread
+//     between them;
 //   * split-K: blocks along grid.z own disjoint K ranges; with S > 1 each
 //     block writes an fp32 partial plane to the workspace and a second small
 //     kernel adds the planes in fixed order (results do not depend on
 //     scheduling), adds the bias and rounds once.
+#include <utility>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,6 +44,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162v_t __attribute__((ext_vector_type(2)));
 
@@ -63,8 +70,48 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
-constexpr int QMM_BN = 128;          // columns per block
-constexpr int QMM_BK = 128;          // K per step
+constexpr int QMM_BK = 128;    // K per step
+
+// The BITS words of one 32-code run (4-byte aligned) in one vector load for
+// BITS <= 4 and two above.
+template <int BITS>
+__device__ __forceinline__ void load_run_words(const uint8_t* src, uint32_t (&w)[BITS]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const uint8_t* s = static_cast<const uint8_t*>(__builtin_assume_aligned(src, 4));
+  constexpr int O = BITS >= 4 ? 4 : 0;
+  constexpr int REST = BITS - O;
+  if constexpr (BITS >= 4) {
+    u32x4 v;
+    __builtin_memcpy(&v, s, 16);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  if constexpr (REST == 3) {
+    u32x3 v;
+    __builtin_memcpy(&v, s + 4 * O, 12);
+    w[O] = v.x; w[O + 1] = v.y; w[O + 2] = v.z;
+  } else if constexpr (REST == 2) {
+    u32x2 v;
+    __builtin_memcpy(&v, s + 4 * O, 8);
+    w[O] = v.x; w[O + 1] = v.y;
+  } else if constexpr (REST == 1) {
+    __builtin_memcpy(&w[O], s + 4 * O, 4);
+  }
+}
+
+// a & 0x0f0f0f0f, opaque to the optimizer (which would otherwise fold the
+// masking into one bit-field extract per code and lose the byte planes)
+__device__ __forceinline__ uint32_t and_nibbles(uint32_t a) {
+  uint32_t r;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+
+template <int I>
+__device__ __forceinline__ float ubyte(uint32_t v) {  // v_cvt_f32_ubyte<I>
+  return static_cast<float>((v >> (8 * I)) & 0xFFu);
+}
 
 // Dequantize codes I and I+1 of a 32-code run into one packed pair.
 template <int BITS, int ACT, int I>
@@ -74,204 +121,271 @@ __device__ __forceinline__ uint32_t dequant2(const uint32_t* w, float s, float z
   return pack2<ACT>(a, b);
 }
 
-// Dequantize the 8 codes [8ks, 8ks+8) of a 32-code run into one operand.
+// Dequantize k-sub KS (codes [8KS, 8KS+8)) of a 32-code run into one MFMA
+// operand: four packed pairs (code 8KS+2j in the low half of dword j).
 template <int BITS, int ACT, int KS>
-__device__ __forceinline__ uint4 dequant8(const uint32_t* w, float s, float z) {
-  return make_uint4(dequant2<BITS, ACT, 8 * KS + 0>(w, s, z), dequant2<BITS, ACT, 8 * KS + 2>(w, s, z),
-                    dequant2<BITS, ACT, 8 * KS + 4>(w, s, z), dequant2<BITS, ACT, 8 * KS + 6>(w, s, z));
+__device__ __forceinline__ uint4 dequant_ksub(const uint32_t (&w)[BITS], float s, float z) {
+  if constexpr (BITS == 4) {
+    // word KS holds the 8 codes as nibbles: split them into two byte planes
+    // (even codes, odd codes) so that every code converts straight from a byte
+    const uint32_t lo = and_nibbles(w[KS]);
+    const uint32_t hi = and_nibbles(w[KS] >> 4);
+    return make_uint4(pack2<ACT>(__builtin_fmaf(s, ubyte<0>(lo), z), __builtin_fmaf(s, ubyte<0>(hi), z)),
+                      pack2<ACT>(__builtin_fmaf(s, ubyte<1>(lo), z), __builtin_fmaf(s, ubyte<1>(hi), z)),
+                      pack2<ACT>(__builtin_fmaf(s, ubyte<2>(lo), z), __builtin_fmaf(s, ubyte<2>(hi), z)),
+                      pack2<ACT>(__builtin_fmaf(s, ubyte<3>(lo), z), __builtin_fmaf(s, ubyte<3>(hi), z)));
+  } else {
+    return make_uint4(dequant2<BITS, ACT, 8 * KS + 0>(w, s, z), dequant2<BITS, ACT, 8 * KS + 2>(w, s, z),
+                      dequant2<BITS, ACT, 8 * KS + 4>(w, s, z), dequant2<BITS, ACT, 8 * KS + 6>(w, s, z));
+  }
 }
 
-// Dequantize k-sub KS (codes [8KS, 8KS+8)) of a 32-code run.
-template <int BITS, int ACT, int KS>
-__device__ __forceinline__ uint4 dequant_ks(const uint32_t* w, float s, float z) {
-  return dequant8<BITS, ACT, KS>(w, s, z);
+// Pair J (codes 8KS+2J and 8KS+2J+1) of k-sub KS of a 32-code run, packed
+// into one operand dword.  For 4-bit codes, lo / hi are the byte planes of
+// word KS (even codes, odd codes), so every code converts straight from a byte.
+template <int BITS, int ACT, int KS, int J>
+__device__ __forceinline__ uint32_t dq_pair(const uint32_t (&w)[BITS], uint32_t lo, uint32_t hi, float s,
+                                            float z) {
+  if constexpr (BITS == 4) {
+    return pack2<ACT>(__builtin_fmaf(s, ubyte<J>(lo), z), __builtin_fmaf(s, ubyte<J>(hi), z));
+  } else {
+    return dequant2<BITS, ACT, 8 * KS + 2 * J>(w, s, z);
+  }
 }
 
-template <int BITS, int ACT>
-__device__ __forceinline__ void dequant_run(const uint32_t* w, float s, float z, uint4 (&b)[4]) {
-  b[0] = dequant8<BITS, ACT, 0>(w, s, z);
-  b[1] = dequant8<BITS, ACT, 1>(w, s, z);
-  b[2] = dequant8<BITS, ACT, 2>(w, s, z);
-  b[3] = dequant8<BITS, ACT, 3>(w, s, z);
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
-// Two waves per SIMD (two blocks per CU): the register budget is 256 per wave.
-template <int BITS, int ACT, int MTT>
-__global__ __launch_bounds__(256, 2) void qmm_kernel(QmmParams p) {
-  constexpr int MROWS = 16 * MTT;
-  constexpr int XCH = MTT;   // 16-byte activation chunks staged per thread per step
-  // two activation stages as separate arrays, so that the compiler can tell
-  // the stage being read from the one being filled
-  __shared__ uint4 stage0[MTT * 16 * 16];
-  __shared__ uint4 stage1[MTT * 16 * 16];
+// One block: 16*MTT rows x 64*NT columns, 4 waves; wave w owns columns
+// [16*NT*w, 16*NT*(w+1)) as NT 16-wide MFMA tiles and all rows.  One block
+// per CU: the register budget is the whole SIMD.
+template <int BITS, int ACT, int MTT, int NT>
+__global__ __launch_bounds__(256, 1) void qmm_kernel(QmmParams p) {
+  constexpr int STAGE = MTT * 16 * 16;   // uint4 per activation stage (16*MTT rows x 256 B)
+  constexpr int MH = MTT > 1 ? MTT / 2 : 1;   // activation fragments are refilled in two halves
+  __shared__ uint4 stage0[STAGE];
+  __shared__ uint4 stage1[STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int fr = lane & 15;           // row / column inside a 16-wide MFMA tile
-  const int g = lane >> 4;            // lane group: K positions [32g, 32g+32)
-  const int n0 = blockIdx.x * QMM_BN;
-  const int m0 = blockIdx.y * MROWS;
+  const int g = lane >> 4;            // lane group: K positions [32g, 32g+32) of a step
+  const int n0 = blockIdx.x * (64 * NT);
+  const int m0 = blockIdx.y * (16 * MTT);
   const int ksteps = (p.K + QMM_BK - 1) / QMM_BK;
   const int s_begin = blockIdx.z * p.ksteps_per_split;
   const int s_end = min(ksteps, s_begin + p.ksteps_per_split);
 
-  // ---- weight rows of this lane (clamped; out-of-range columns get s=z=0)
-  int ncol[2];
-  bool nok[2];
+  // ---- this lane's weight rows (clamped; columns past N get s = z = 0)
+  int64_t wrow[NT], szrow[NT];
+  uint32_t nok[NT];   // all ones for a real column, 0 past N
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int n = n0 + 32 * wave + 16 * nt + fr;
-    nok[nt] = n < p.N;
-    ncol[nt] = nok[nt] ? n : p.N - 1;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * NT * wave + 16 * nt + fr;
+    nok[nt] = 0u - static_cast<uint32_t>(n < p.N);
+    const int nc = min(n, p.N - 1);
+    wrow[nt] = static_cast<int64_t>(nc) * p.row_bytes;
+    szrow[nt] = static_cast<int64_t>(nc) * p.groups;
   }
+  using bits_t = typename Act<ACT>::bits_t;
+  const bits_t* sc_bits = static_cast<const bits_t*>(p.scales);
+  const bits_t* ze_bits = static_cast<const bits_t*>(p.zeros);
 
-  auto load_codes = [&](int step, uint32_t (&w)[2][BITS], uint32_t (&sb)[2], uint32_t (&zb)[2],
-                        bool& kok) {
-    const int k = step * QMM_BK + 32 * g;
-    kok = k < p.K;
-    const int kc = kok ? k : p.K - 32;
+  // Codes of one step for this lane: NT runs of 32 codes, their scale and
+  // zero (raw bits), and a mask that is all ones when the step's K range of
+  // this lane group is real.  Masks, not branches: the loop stays straight.
+  struct Codes {
+    uint32_t w[NT][BITS];
+    uint32_t s[NT], z[NT];
+    uint32_t ok;
+  };
+  auto load_codes = [&](int step, Codes& c) {
+    const int st = min(step, s_end - 1);
+    const int k = st * QMM_BK + 32 * g;
+    c.ok = 0u - static_cast<uint32_t>((step < s_end) & (k < p.K));
+    const int kc = min(k, p.K - 32);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(
-          p.packed + static_cast<int64_t>(ncol[nt]) * p.row_bytes + (kc >> 3) * BITS);
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w[nt][i] = src[i];
-      const int64_t gi = static_cast<int64_t>(ncol[nt]) * p.groups + (kc >> p.group_shift);
-      sb[nt] = static_cast<const typename Act<ACT>::bits_t*>(p.scales)[gi];
-      zb[nt] = static_cast<const typename Act<ACT>::bits_t*>(p.zeros)[gi];
+    for (int nt = 0; nt < NT; ++nt) {
+      load_run_words<BITS>(p.packed + wrow[nt] + (kc >> 3) * BITS, c.w[nt]);
+      const int64_t gi = szrow[nt] + (kc >> p.group_shift);
+      c.s[nt] = sc_bits[gi];
+      c.z[nt] = ze_bits[gi];
     }
   };
-  auto dequant = [&](const uint32_t (&w)[2][BITS], const uint32_t (&sb)[2],
-                     const uint32_t (&zb)[2], bool kok, uint4 (&b)[2][4]) {
+  auto scale_zero = [&](const Codes& c, float (&sv)[NT], float (&zv)[NT]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const bool ok = kok && nok[nt];
-      const float s = ok ? act_bits_to_float<ACT>(sb[nt]) : 0.0f;
-      const float z = ok ? act_bits_to_float<ACT>(zb[nt]) : 0.0f;
-      dequant_run<BITS, ACT>(w[nt], s, z, b[nt]);
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t ok = c.ok & nok[nt];
+      sv[nt] = act_bits_to_float<ACT>(c.s[nt] & ok);   // zero bits -> +0.0f
+      zv[nt] = act_bits_to_float<ACT>(c.z[nt] & ok);
     }
   };
+
   // Activation stage: the 16*MTT x 128 tile of one step, rows of 256 bytes
   // (16 chunks of 8 elements) with chunk c of row r stored at position
-  // c ^ (r & 15) -- the 16 lanes that read one k-sub of an MFMA tile then hit
-  // 16 different 16-byte bank groups.  It is filled with direct global->LDS
-  // loads (lane i of a wave lands at dst + 16 i), so it costs no registers:
-  // wave w's load i covers rows 4*(4i + w) .. +3, and each lane fetches the
-  // chunk that belongs at its position.  Rows past M and chunks past K read a
-  // clamped in-range address: a row past M only feeds output rows that are
-  // never stored, and past K the weights are dequantized with s = z = 0.
-  auto load_x_lds = [&](int step, uint4* stage) {
-    uint8_t* base = reinterpret_cast<uint8_t*>(stage);
+  // c ^ (r & 15), so that the 16 lanes reading one k-sub of an MFMA tile hit
+  // 16 different 16-byte bank groups.  Load i of wave w covers rows
+  // 4*(4i + w) .. +3: lane l fetches the chunk that belongs at position l & 15
+  // of row 4*(4i + w) + l/16, and later stores it at byte 16 l of those four
+  // rows.  Rows past M and chunks past K read a clamped in-range address: such
+  // a row only feeds output rows that are never stored, and past K the
+  // weights are dequantized with s = z = 0.
+  const uint16_t* xrow[MTT];
+  int xchunk[MTT];
 #pragma unroll
-    for (int i = 0; i < MTT; ++i) {
-      const int r0 = 4 * (4 * i + wave);
-      const int row = r0 + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 15);
-      const int grow = min(m0 + row, p.M - 1);
-      const int k = min(step * QMM_BK + 8 * c, p.K - 8);
-      const uint16_t* src = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(grow) * p.K + k;
-      __builtin_amdgcn_global_load_lds(src, base + r0 * 256, 16, 0, 0);
-    }
+  for (int i = 0; i < MTT; ++i) {
+    const int row = 4 * (4 * i + wave) + (lane >> 4);
+    xchunk[i] = 8 * ((lane & 15) ^ (row & 15));
+    xrow[i] = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.K;
+  }
+  // (native vectors: HIP's uint4 is a struct whose copies become memcpys
+  // that keep these arrays out of registers)
+  auto load_x = [&](int step, u32x4_t (&xr)[MTT]) {
+    const int kb = min(step, s_end - 1) * QMM_BK;
+#pragma unroll
+    for (int i = 0; i < MTT; ++i)
+      xr[i] = *reinterpret_cast<const u32x4_t*>(xrow[i] + min(kb + xchunk[i], p.K - 8));
+  };
+  auto store_x = [&](const u32x4_t (&xr)[MTT], uint4* stage) {
+#pragma unroll
+    for (int i = 0; i < MTT; ++i) reinterpret_cast<u32x4_t*>(stage)[(4 * i + wave) * 64 + lane] = xr[i];
   };
 
-  float4_t acc[MTT][2];
+  float4_t acc[MTT][NT];
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t bw[NT][4][4];   // weight operands of the current step: [column tile][k-sub][dword]
+  uint4 af[MTT];           // activation operands of one k-sub: [row tile]
 
-  // activation operands of k-sub ks (16 rows per MFMA tile, 8 K each)
-  auto read_a = [&](const uint8_t* abase, int ks, uint4 (&a)[MTT]) {
-#pragma unroll
-    for (int mt = 0; mt < MTT; ++mt)
-      a[mt] = *reinterpret_cast<const uint4*>(abase + (16 * mt + fr) * 256 +
-                                              (((4 * g + ks) ^ fr) << 4));
+  // activation operands of row tiles [MT0, MT1) for k-sub KS
+  auto read_a = [&](const uint4* stage, auto KSc, auto MT0c, auto MT1c) {
+    constexpr int KS = decltype(KSc)::value;
+    static_for<decltype(MT1c)::value - decltype(MT0c)::value>([&](auto ic) {
+      constexpr int mt = decltype(MT0c)::value + decltype(ic)::value;
+      af[mt] = stage[(16 * mt + fr) * 16 + ((4 * g + KS) ^ fr)];
+    });
   };
-  auto mma = [&](const uint4 (&bc)[2][4], int ks, const uint4 (&a)[MTT]) {
-#pragma unroll
-    for (int mt = 0; mt < MTT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32<ACT>(a[mt], bc[nt][ks], acc[mt][nt]);
+  using I0 = std::integral_constant<int, 0>;
+  using IMH = std::integral_constant<int, MH>;
+  using IMTT = std::integral_constant<int, MTT>;
+
+  // One phase: the MFMAs of k-sub KS in row-tile-major order, with the
+  // dequantization of k-sub DKS of code set C spread evenly between them (one
+  // packed pair at a time), and the activation operands of k-sub NKS (from
+  // stage NS, if NKS >= 0) read in two halves as soon as the MFMAs that use
+  // their registers have been issued.  Scheduling barriers pin this order:
+  // with one wave per SIMD, the MFMA pipe stays busy only if the VALU work
+  // sits between the MFMAs rather than in clusters.
+  auto phase = [&](auto KSc, auto DKSc, const Codes& C, const float (&sv)[NT], const float (&zv)[NT],
+                   const uint4* ns, auto NKSc) {
+    constexpr int KS = decltype(KSc)::value;
+    constexpr int DKS = decltype(DKSc)::value;
+    constexpr int NKS = decltype(NKSc)::value;
+    constexpr int NMF = MTT * NT;
+    constexpr int NPC = NT * 4;
+    uint32_t lo[NT], hi[NT];
+    static_for<NMF>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int mt = i / NT, nt = i % NT;
+      acc[mt][nt] = mfma16x16x32<ACT>(af[mt], make_uint4(bw[nt][KS][0], bw[nt][KS][1], bw[nt][KS][2],
+                                                         bw[nt][KS][3]), acc[mt][nt]);
+      constexpr int p0 = i * NPC / NMF, p1 = (i + 1) * NPC / NMF;
+      static_for<p1 - p0>([&](auto jc) {
+        constexpr int pc = p0 + decltype(jc)::value;
+        constexpr int c = pc / 4, j = pc % 4;
+        if constexpr (BITS == 4 && j == 0) {
+          lo[c] = and_nibbles(C.w[c][DKS]);
+          hi[c] = and_nibbles(C.w[c][DKS] >> 4);
+        }
+        bw[c][DKS][j] = dq_pair<BITS, ACT, DKS, j>(C.w[c], lo[c], hi[c], sv[c], zv[c]);
+      });
+      if constexpr (NKS >= 0 && i == MH * NT - 1)
+        read_a(ns, std::integral_constant<int, NKS>{}, I0{}, IMH{});
+      if constexpr (NKS >= 0 && MH < MTT && i == NMF - 1)
+        read_a(ns, std::integral_constant<int, NKS>{}, IMH{}, IMTT{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  using K3 = std::integral_constant<int, 3>;
 
-  if (s_begin < s_end) {
-    // Pipeline: codes are fetched two steps ahead (register sets A and B
-    // alternate), activations one step ahead (LDS stages 0 and 1 alternate).
-    // The weight operands live in one register set: right after the MFMAs of
-    // k-sub ks are issued, k-sub ks of the next step is dequantized into the
-    // same registers, so dequantization overlaps the remaining MFMAs.  The
-    // loop always runs an even number of steps: a step past the block's
-    // range loads clamped, in-range addresses and multiplies by weights
-    // dequantized with s = z = 0, so it adds nothing -- keeping the loop body
-    // free of branches lets the accumulators stay in place.
-    uint32_t wa[2][BITS], sa[2], za[2], wb[2][BITS], sbb[2], zbb[2];
-    bool ka, kb;
-    uint4 bop[2][4];
-    auto load_step = [&](int step, uint32_t (&w)[2][BITS], uint32_t (&sb)[2], uint32_t (&zb)[2],
-                         bool& kok) {
-      load_codes(min(step, s_end - 1), w, sb, zb, kok);
-      kok = kok && step < s_end;
-    };
-    auto scale_zero = [&](const uint32_t (&sb)[2], const uint32_t (&zb)[2], bool kok, float (&sv)[2],
-                          float (&zv)[2]) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const bool ok = kok && nok[nt];
-        sv[nt] = ok ? act_bits_to_float<ACT>(sb[nt]) : 0.0f;
-        zv[nt] = ok ? act_bits_to_float<ACT>(zb[nt]) : 0.0f;
-      }
-    };
-    load_step(s_begin, wa, sa, za, ka);
-    load_x_lds(s_begin, stage0);
-    load_step(s_begin + 1, wb, sbb, zbb, kb);
-    dequant(wa, sa, za, ka, bop);
-    __builtin_amdgcn_s_waitcnt(0);    // stage 0 has landed in LDS
-    __syncthreads();
-
-    // One K step: multiply `read` x bop; fetch the codes of step+2 into the
-    // register set that just became free and the activations of step+1 into
-    // `fill`; dequantize step+1 (codes already in `wn`) into bop, k-sub by
-    // k-sub, behind the MFMAs that last read it.
-#define LOWBIT_QMM_DQ(KS, WN, SV, ZV)                                                         \
-    bop[0][KS] = dequant_ks<BITS, ACT, KS>(WN[0], SV[0], ZV[0]);                              \
-    bop[1][KS] = dequant_ks<BITS, ACT, KS>(WN[1], SV[1], ZV[1]);
-#define LOWBIT_QMM_STEP(STEP, READ, FILL, WN, SN, ZN, KN, WF, SF, ZF, KF)                     \
-    {                                                                                        \
-      load_step((STEP) + 2, WF, SF, ZF, KF);                                                 \
-      load_x_lds(min((STEP) + 1, s_end - 1), FILL);                                          \
-      const uint8_t* abase = reinterpret_cast<const uint8_t*>(READ);                         \
-      float sv[2], zv[2];                                                                    \
-      scale_zero(SN, ZN, KN, sv, zv);                                                        \
-      uint4 a0[MTT], a1[MTT];                                                                \
-      read_a(abase, 0, a0);                                                                  \
-      read_a(abase, 1, a1);                                                                  \
-      mma(bop, 0, a0);                                                                       \
-      LOWBIT_QMM_DQ(0, WN, sv, zv)                                                           \
-      read_a(abase, 2, a0);                                                                  \
-      mma(bop, 1, a1);                                                                       \
-      LOWBIT_QMM_DQ(1, WN, sv, zv)                                                           \
-      read_a(abase, 3, a1);                                                                  \
-      mma(bop, 2, a0);                                                                       \
-      LOWBIT_QMM_DQ(2, WN, sv, zv)                                                           \
-      mma(bop, 3, a1);                                                                       \
-      LOWBIT_QMM_DQ(3, WN, sv, zv)                                                           \
-      __builtin_amdgcn_s_waitcnt(0); /* next stage landed; this one fully read */            \
-      __syncthreads();                                                                       \
-    }
-    for (int step = s_begin; step < s_end; step += 2) {
-      LOWBIT_QMM_STEP(step, stage0, stage1, wb, sbb, zbb, kb, wa, sa, za, ka)
-      LOWBIT_QMM_STEP(step + 1, stage1, stage0, wa, sa, za, ka, wb, sbb, zbb, kb)
-    }
-#undef LOWBIT_QMM_STEP
-#undef LOWBIT_QMM_DQ
+  // Pipeline over K steps, with two register sets (A, B) for codes and
+  // activations: step t reads LDS stage t%2; in its first phase it loads the
+  // activations of step t+2 and, once k-sub 3 of its own codes is
+  // dequantized, the codes of step t+2; it stores the activations of step
+  // t+1 into the other stage and meets the other waves once that stage is
+  // written and its own is fully read, then reads the first operands of
+  // step t+1 during its last phase.  Weight operands are dequantized one
+  // k-sub ahead, in place: k-sub 3 of step t during phase 0, k-subs 0..2 of
+  // step t+1 during phases 1..3.  All loads are ordinary loads that
+  // complete in order, so every use waits only for the loads it needs.
+#define LOWBIT_QMM_STEP(S_, SR, SW, XLD, XST, CUR, NXT)                                       \
+  {                                                                                           \
+    load_x((S_) + 2, XLD);                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    {                                                                                         \
+      float sv[NT], zv[NT];                                                                   \
+      scale_zero(CUR, sv, zv);                                                                \
+      phase(K0{}, K3{}, CUR, sv, zv, SR, K1{});                                               \
+    }                                                                                         \
+    load_codes((S_) + 2, CUR);                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    float sv[NT], zv[NT];                                                                     \
+    scale_zero(NXT, sv, zv);                                                                  \
+    phase(K1{}, K0{}, NXT, sv, zv, SR, K2{});                                                 \
+    store_x(XST, SW);                                                                         \
+    phase(K2{}, K1{}, NXT, sv, zv, SR, K3{});                                                 \
+    __syncthreads(); /* stage S_+1 written by every wave; stage S_ fully read */              \
+    phase(K3{}, K2{}, NXT, sv, zv, SW, K0{});                                                 \
   }
+
+  Codes ca, cb;
+  u32x4_t xa[MTT], xb[MTT];
+  load_x(s_begin, xa);
+  load_x(s_begin + 1, xb);
+  load_codes(s_begin, ca);
+  load_codes(s_begin + 1, cb);
+  store_x(xa, stage0);
+  {
+    float sv[NT], zv[NT];
+    scale_zero(ca, sv, zv);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint4 b0 = dequant_ksub<BITS, ACT, 0>(ca.w[nt], sv[nt], zv[nt]);
+      const uint4 b1 = dequant_ksub<BITS, ACT, 1>(ca.w[nt], sv[nt], zv[nt]);
+      const uint4 b2 = dequant_ksub<BITS, ACT, 2>(ca.w[nt], sv[nt], zv[nt]);
+      bw[nt][0][0] = b0.x; bw[nt][0][1] = b0.y; bw[nt][0][2] = b0.z; bw[nt][0][3] = b0.w;
+      bw[nt][1][0] = b1.x; bw[nt][1][1] = b1.y; bw[nt][1][2] = b1.z; bw[nt][1][3] = b1.w;
+      bw[nt][2][0] = b2.x; bw[nt][2][1] = b2.y; bw[nt][2][2] = b2.z; bw[nt][2][3] = b2.w;
+    }
+  }
+  __syncthreads();
+  read_a(stage0, K0{}, I0{}, IMTT{});
+  int s = s_begin;
+  for (; s + 2 <= s_end; s += 2) {
+    LOWBIT_QMM_STEP(s, stage0, stage1, xa, xb, ca, cb)
+    LOWBIT_QMM_STEP(s + 1, stage1, stage0, xb, xa, cb, ca)
+  }
+  if (s < s_end) LOWBIT_QMM_STEP(s, stage0, stage1, xa, xb, ca, cb)
+#undef LOWBIT_QMM_STEP
 
   // ---- epilogue.  Lane holds D[4*g + r][fr] of each 16x16 tile.
   if (gridDim.z == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = n0 + 32 * wave + 16 * nt + fr;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 16 * NT * wave + 16 * nt + fr;
       if (n >= p.N) continue;
       const float bias = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
 #pragma unroll
@@ -289,8 +403,8 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(QmmParams p) {
   // workspace; qmm_reduce adds the planes in order.
   float* part = p.partials + static_cast<int64_t>(blockIdx.z) * p.M * p.N;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int n = n0 + 32 * wave + 16 * nt + fr;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * NT * wave + 16 * nt + fr;
     if (n >= p.N) continue;
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt)
@@ -340,18 +454,22 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, int splits
 }
 
 template <int ACT, int MTT>
-static hipError_t launch_mtt(const QmmParams& p, dim3 grid, hipStream_t s) {
-  qmm_kernel<LOWBIT_BITS, ACT, MTT><<<grid, dim3(256), 0, s>>>(p);
+static hipError_t launch_mtt(const QmmParams& p, int nt, dim3 grid, hipStream_t s) {
+  switch (nt) {
+    case 2: qmm_kernel<LOWBIT_BITS, ACT, MTT, 2><<<grid, dim3(256), 0, s>>>(p); break;
+    case 4: qmm_kernel<LOWBIT_BITS, ACT, MTT, 4><<<grid, dim3(256), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <int ACT>
-static hipError_t launch_act(const QmmParams& p, int mtt, dim3 grid, hipStream_t s) {
+static hipError_t launch_act(const QmmParams& p, int mtt, int nt, dim3 grid, hipStream_t s) {
   switch (mtt) {
-    case 1: return launch_mtt<ACT, 1>(p, grid, s);
-    case 2: return launch_mtt<ACT, 2>(p, grid, s);
-    case 4: return launch_mtt<ACT, 4>(p, grid, s);
-    case 8: return launch_mtt<ACT, 8>(p, grid, s);
+    case 1: return launch_mtt<ACT, 1>(p, nt, grid, s);
+    case 2: return launch_mtt<ACT, 2>(p, nt, grid, s);
+    case 4: return launch_mtt<ACT, 4>(p, nt, grid, s);
+    case 8: return launch_mtt<ACT, 8>(p, nt, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -362,8 +480,8 @@ hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLa
                                                  hipStream_t s) {
   hipError_t e;
   switch (act) {
-    case ACT_F16: e = launch_act<ACT_F16>(p, l.mtt, l.grid, s); break;
-    case ACT_BF16: e = launch_act<ACT_BF16>(p, l.mtt, l.grid, s); break;
+    case ACT_F16: e = launch_act<ACT_F16>(p, l.mtt, l.nt, l.grid, s); break;
+    case ACT_BF16: e = launch_act<ACT_BF16>(p, l.mtt, l.nt, l.grid, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || l.grid.z == 1) return e;

@@ -4,10 +4,12 @@
 // optimization" (Summary) streams packed rows and applies the N x num_groups
 // scales and zeros inside the dot product.  This kernel keeps that idea and is
 // laid out for CDNA4:
-//   * a row's codes are cut into 128-code units; a unit of b-bit codes is
-//     exactly b x 16 bytes, fetched with b 128-bit loads;
+//   * a row's codes are cut into 32-code runs; a run of b-bit codes is
+//     exactly b 32-bit words, fetched with one or two vector loads;
 //   * 2^lpr_shift lanes of a wavefront share a group of R rows; in round t
-//     lane l owns unit t*lanes + l of each of its R rows;
+//     lane l owns runs 4*t*lanes + l + lanes*j (j = 0..3) of each of its R
+//     rows, so that each load instruction of the group reads one contiguous
+//     span of the packed row;
 //   * the block stages the activations of the round once in LDS, already
 //     rearranged into the operand pairs the unpack plan needs, together with
 //     each 32-code run's activation sum X and constant part C; activation
@@ -19,7 +21,7 @@
 //   * per 32-code run (which never crosses a group):
 //       y += s * (sum_k x_k q_k) + z * X,  sum_k x_k q_k = P - C;
 //   * the R row partial sums of the lanes of a row group are combined with
-//     lane shuffles; bias is added in fp32 and the result rounded once.
+//     DPP lane moves; bias is added in fp32 and the result rounded once.
 #include "device_common.h"
 #include "kernels.h"
 #include "qmv_plan.h"
@@ -153,34 +155,34 @@ __device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) 
 
 // ----------------------------------------------------------------- loads --
 
-// The 4*BITS words of 128-code unit `u` of one row.  FAST: the unit is whole
-// and 16-byte aligned (b 128-bit loads).  Otherwise runs past the row end
-// (nsub of them are valid) re-read the last valid run and are zeroed.
-template <int BITS, bool FAST>
-__device__ __forceinline__ void load_unit(const uint8_t* rowp, int nsub, uint32_t (&d)[4 * BITS]) {
-  if constexpr (FAST) {
-    const uint4* s = reinterpret_cast<const uint4*>(rowp);
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) {
-      const uint4 v = s[i];
-      d[4 * i + 0] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
-    }
-  } else {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(rowp);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int jj = min(j, nsub - 1);
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) {
-        const uint32_t v = s[jj * BITS + i];
-        d[j * BITS + i] = (j < nsub) ? v : 0u;
-      }
-    }
+// The BITS words of one 32-code run (4-byte aligned): one vector load for
+// BITS <= 4, two above.
+template <int BITS>
+__device__ __forceinline__ void load_run(const uint8_t* src, uint32_t* w) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const uint8_t* s = static_cast<const uint8_t*>(__builtin_assume_aligned(src, 4));
+  constexpr int O = BITS >= 4 ? 4 : 0;
+  constexpr int REST = BITS - O;
+  if constexpr (BITS >= 4) {
+    u32x4 v;
+    __builtin_memcpy(&v, s, 16);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  if constexpr (REST == 3) {
+    u32x3 v;
+    __builtin_memcpy(&v, s + 4 * O, 12);
+    w[O] = v.x; w[O + 1] = v.y; w[O + 2] = v.z;
+  } else if constexpr (REST == 2) {
+    u32x2 v;
+    __builtin_memcpy(&v, s + 4 * O, 8);
+    w[O] = v.x; w[O + 1] = v.y;
+  } else if constexpr (REST == 1) {
+    __builtin_memcpy(&w[O], s + 4 * O, 4);
   }
 }
 
-// 32 activations starting at element `off` (always a valid address); the
-// caller zeroes them when the run lies outside x.
 template <int ACT>
 __device__ __forceinline__ void load_raw_run(const void* x, int64_t off,
                                              uint32_t (&raw)[RawWords<ACT>::n]) {
@@ -194,47 +196,20 @@ __device__ __forceinline__ void load_raw_run(const void* x, int64_t off,
   }
 }
 
-// Raw bits of the scales (or zeros) of the 4 runs of unit u of one row; run j
-// uses group (u*128 + 32j) / GROUP.  FAST (K % 128 == 0): the unit's groups
-// are one aligned vector of max(1, 128/GROUP) elements.  Conversion to fp32
-// happens at first use, so these loads never force an early wait.
-template <int ACT, int GROUP, bool FAST>
-__device__ __forceinline__ void load_unit_sz(const void* base, int64_t row_off, int u, int groups,
-                                             uint32_t (&v)[4]) {
-  constexpr int NG = GROUP >= 128 ? 1 : 128 / GROUP;
-  using T = typename Act<ACT>::bits_t;
-  const T* p = static_cast<const T*>(base) + row_off;
-  if constexpr (FAST) {
-    const int g0 = GROUP == 256 ? (u >> 1) : u * NG;
-    T t[NG];
-    if constexpr (NG * sizeof(T) == 16) {
-      const uint4 a = *reinterpret_cast<const uint4*>(p + g0);
-      __builtin_memcpy(t, &a, 16);
-    } else if constexpr (NG * sizeof(T) == 8) {
-      const uint2 a = *reinterpret_cast<const uint2*>(p + g0);
-      __builtin_memcpy(t, &a, 8);
-    } else if constexpr (NG * sizeof(T) == 4) {
-      const uint32_t a = *reinterpret_cast<const uint32_t*>(p + g0);
-      __builtin_memcpy(t, &a, 4);
-    } else {
-      t[0] = p[g0];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = t[(j * 32) / GROUP % NG];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = p[min((u * 128 + 32 * j) / GROUP, groups - 1)];
-  }
-}
-
-// ---------------------------------------------------------------- kernel --
-
-template <int BITS, int GROUP, int ACT, int MT, bool FAST>
+// Decode kernel: rows are processed by groups of `lanes` lanes (a power of
+// two <= 64); each lane takes four 32-code runs of the row per round.  Runs
+// are dealt out interleaved -- in round t, slot j of lane l is run
+// 4*t*lanes + l + lanes*j -- so that every weight load instruction of a
+// row group reads one contiguous span of the packed row.  Each lane
+// accumulates, per run, P = sum x*q against activations staged in LDS in the
+// form its bit width needs, then y += s*P + z*X (X = sum of the run's x).
+template <int BITS, int GROUP, int ACT, int MT>
 __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   extern __shared__ uint4 stage[];
   constexpr int R = (MT == 1) ? 2 : 1;          // rows per row group
   constexpr int RAW = RawWords<ACT>::n;
   constexpr int QD = RunQuads<ACT, BITS>::n;    // staged quads per run
+  constexpr int GSHIFT = GROUP == 32 ? 5 : GROUP == 64 ? 6 : GROUP == 128 ? 7 : 8;
 
   const int tid = threadIdx.x;
   const int lanes = 1 << p.lpr_shift;
@@ -245,7 +220,8 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   const int m0 = blockIdx.y * MT;
   const int mcount = min(MT, p.M - m0);
   const int nruns = MT * 4 * lanes;              // staged runs per round
-  const int rounds = (p.units + lanes - 1) / lanes;
+  const int runs = p.K >> 5;                     // 32-code runs per row
+  const int rounds = (runs + 4 * lanes - 1) / (4 * lanes);
 
   float acc[R][MT];
 #pragma unroll
@@ -254,18 +230,19 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
   for (int t = 0; t < rounds; ++t) {
-    const int ubase = t * lanes;
-    // -- activation loads for this thread's first staged run (issued first)
+    const int rbase = 4 * t * lanes;             // first run of the round
+    // -- activation loads for this thread's first staged run (issued first).
+    // Staged run rr: activation row m, slot j, lane-in-group ul.
     auto run_coords = [&](int rr, int& m, int& ul, int& j) {
       m = rr / (4 * lanes);
       const int rem = rr - m * 4 * lanes;
-      ul = rem >> 2;
-      j = rem & 3;
+      ul = rem & (lanes - 1);
+      j = rem >> p.lpr_shift;
     };
     auto run_load = [&](int rr, uint32_t (&raw)[RAW]) {
       int m, ul, j;
       run_coords(rr, m, ul, j);
-      const int k = (ubase + ul) * 128 + 32 * j;
+      const int k = (rbase + ul + lanes * j) * 32;
       const bool valid = rr < nruns && m < mcount && k < p.K;
       load_raw_run<ACT>(p.x, valid ? static_cast<int64_t>(m0 + m) * p.K + k : 0, raw);
       return valid;
@@ -273,25 +250,32 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
     uint32_t raw[RAW];
     const bool raw_valid = run_load(tid, raw);
 
-    // -- weights, scales and zeros of this lane's unit (addresses clamped to
-    // the matrix; rows past N and units past K get zero scale and zero)
-    const int u = ubase + lane;
-    const bool active = u < p.units;
-    const int uc = active ? u : p.units - 1;
-    const int nsub = FAST ? 4 : min(4, (p.K - uc * 128) >> 5);
+    // -- weights, scales and zeros of this lane's four runs (addresses
+    // clamped to the matrix; rows past N and runs past K get zero scale and
+    // zero).  Scales and zeros stay raw bits until first use, so these loads
+    // never force an early wait.
     uint32_t d[R][4 * BITS];
     uint32_t sb[R][4], zb[R][4];
+    bool rok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rok[j] = rbase + lane + lanes * j < runs;
+    using T = typename Act<ACT>::bits_t;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int nc = min(n_base + r, p.N - 1);
-      load_unit<BITS, FAST>(p.packed + static_cast<int64_t>(nc) * p.row_bytes +
-                                static_cast<int64_t>(uc) * 16 * BITS, nsub, d[r]);
+      const uint8_t* rowp = p.packed + static_cast<int64_t>(nc) * p.row_bytes;
       const int64_t ro = static_cast<int64_t>(nc) * p.groups;
-      load_unit_sz<ACT, GROUP, FAST>(p.scales, ro, uc, p.groups, sb[r]);
-      load_unit_sz<ACT, GROUP, FAST>(p.zeros, ro, uc, p.groups, zb[r]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int run = min(rbase + lane + lanes * j, runs - 1);
+        load_run<BITS>(rowp + static_cast<int64_t>(run) * 4 * BITS, &d[r][j * BITS]);
+        const int64_t gi = ro + ((run * 32) >> GSHIFT);
+        sb[r][j] = static_cast<const T*>(p.scales)[gi];
+        zb[r][j] = static_cast<const T*>(p.zeros)[gi];
+      }
     }
 
-    // -- stage the round's activations: layout [m][j][quad][unit-in-round].
+    // -- stage the round's activations: layout [m][j][quad][lane-in-group].
     // The thread's first run (loaded above, before the weights) is staged
     // outside the loop so that only the activation loads must have landed.
     // (Threads without a run write to a scratch slot past the stage, which
@@ -318,7 +302,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
     __syncthreads();
 
     // -- compute (runs past K and rows past M hold zero activations, and
-    // clamped rows/units have zero scale and zero, so they add nothing)
+    // clamped rows/runs have zero scale and zero, so they add nothing)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -333,7 +317,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float dq = run_dot<ACT, BITS>(&d[r][j * BITS], xs);
-          const bool ok = active && n_base + r < p.N;
+          const bool ok = rok[j] && n_base + r < p.N;
           const float sv = ok ? act_bits_to_float<ACT>(sb[r][j]) : 0.0f;
           const float zv = ok ? act_bits_to_float<ACT>(zb[r][j]) : 0.0f;
           acc[r][m] = __builtin_fmaf(sv, dq, acc[r][m]);
@@ -370,11 +354,7 @@ static hipError_t launch_one(const QmvParams& p, const QmvLaunch& l, hipStream_t
   // staged runs plus one scratch run for threads without a run
   const size_t lds = (static_cast<size_t>(MT) * 4 * (size_t(1) << p.lpr_shift) + 1) *
                      RunQuads<ACT, LOWBIT_BITS>::n * 16;
-  if (p.aligned16 && p.sz_vec) {
-    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, true><<<l.grid, l.block, lds, s>>>(p);
-  } else {
-    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, false><<<l.grid, l.block, lds, s>>>(p);
-  }
+  qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT><<<l.grid, l.block, lds, s>>>(p);
   return hipGetLastError();
 }
 
