@@ -38,6 +38,13 @@ struct QmvParams {
   int aligned16;          // row_bytes % 16 == 0 (every row starts 16-byte aligned)
   int sz_vec;             // K % 128 == 0: a unit's scales/zeros are one aligned vector
 };
+// Rows per row group of the decode kernel for one activation row per pass:
+// two rows for 1, 2, 3 and 5-bit codes, one for 4, 6 and 7 bits (measured on
+// MI355X at K = N = 4096: each choice is 0.1-0.5 us faster than the other
+// there); one row whenever several activation rows share a pass.
+constexpr int qmv_rows_per_group(int bits, int mt) {
+  return (mt == 1 && (bits <= 3 || bits == 5)) ? 2 : 1;
+}
 struct QmvLaunch {
   dim3 grid, block;
   int mt;                 // activation rows per pass: 1, 2 or 4

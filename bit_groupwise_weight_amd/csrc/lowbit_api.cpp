@@ -159,7 +159,7 @@ lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, co
   if (M >= 2 && 2 * per_row <= kQmvStageBudget) l.mt = 2;
   if (M >= 3 && 4 * per_row <= kQmvStageBudget) l.mt = 4;
   if (per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
-  const int R = (l.mt == 1) ? 2 : 1;
+  const int R = lowbit::qmv_rows_per_group(bits, l.mt);
 
   // Block size: 256 threads unless that leaves fewer blocks than CUs.
   int threads = env_int("LOWBIT_QMV_BLOCK", 0);

@@ -206,7 +206,7 @@ __device__ __forceinline__ void load_raw_run(const void* x, int64_t off,
 template <int BITS, int GROUP, int ACT, int MT>
 __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   extern __shared__ uint4 stage[];
-  constexpr int R = (MT == 1) ? 2 : 1;          // rows per row group
+  constexpr int R = qmv_rows_per_group(BITS, MT);   // rows per row group
   constexpr int RAW = RawWords<ACT>::n;
   constexpr int QD = RunQuads<ACT, BITS>::n;    // staged quads per run
   constexpr int GSHIFT = GROUP == 32 ? 5 : GROUP == 64 ? 6 : GROUP == 128 ? 7 : 8;
