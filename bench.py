@@ -159,6 +159,60 @@ def time_eager(p, reps, stream):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+# Llama-3.1-8B decoder layer linears (name, N, K), M = 1.
+LAYER_SHAPES = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
+                ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
+LAYER_BITS, LAYER_GROUP = 4, 64
+
+
+def prepare_layer(copies, dev):
+    """One decoder layer's seven linears (seeded N(0, 0.02) weights, quantized on
+    the GPU), `copies` independent weight copies, fp16 activations."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    gen = torch.Generator().manual_seed(1234)
+    lin = {}
+    for name, N, K in LAYER_SHAPES:
+        W = (torch.randn((N, K), generator=gen) * 0.02).to(dev)
+        packed, s, z, _ = lb.lowbit_quantize_pack(W, LAYER_BITS, LAYER_GROUP, torch.float16)
+        del W
+        lin[name] = [(packed, s, z)] + [(packed.clone(), s.clone(), z.clone()) for _ in range(copies - 1)]
+    xs = {K: torch.randn((1, K), generator=gen).to(torch.float16).to(dev) for K in (4096, 14336)}
+    ys = {name: torch.empty((1, N), dtype=torch.float16, device=dev) for name, N, _ in LAYER_SHAPES}
+    return {"lin": lin, "x": xs, "y": ys, "copies": copies}
+
+
+def layer_bytes() -> int:
+    return sum(N * K * LAYER_BITS // 8 + 2 * N * (K // LAYER_GROUP) * 2 + 2 * K + 2 * N
+               for _, N, K in LAYER_SHAPES)
+
+
+def layer_separate(L, i, stream):
+    """The seven linears as seven launches."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    c = i % L["copies"]
+    for name, N, K in LAYER_SHAPES:
+        packed, s, z = L["lin"][name][c]
+        lb.lowbit_linear(L["x"][K], packed, s, z, None, LAYER_BITS, LAYER_GROUP, y=L["y"][name],
+                         stream=stream)
+
+
+def layer_fused(L, i, stream):
+    """The same linears as four launches: q/k/v together, o, gate/up together, down."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    c = i % L["copies"]
+
+    def item(name, K):
+        packed, s, z = L["lin"][name][c]
+        return (L["x"][K], packed, s, z, None, L["y"][name])
+
+    lb.lowbit_linear_multi([item("q", 4096), item("k", 4096), item("v", 4096)], LAYER_BITS,
+                           LAYER_GROUP, stream=stream)
+    lb.lowbit_linear_multi([item("o", 4096)], LAYER_BITS, LAYER_GROUP, stream=stream)
+    lb.lowbit_linear_multi([item("gate", 4096), item("up", 4096)], LAYER_BITS, LAYER_GROUP,
+                           stream=stream)
+    lb.lowbit_linear_multi([item("down", 14336)], LAYER_BITS, LAYER_GROUP, stream=stream)
+
+
 def cpu_baseline(cases, reps):
     """The CPU oracle's linear (fp64 dequant + matmul) timed on this host."""
     import oracle
@@ -273,6 +327,28 @@ def main():
         qmm.append({"K": c.K, "N": c.N, "M": c.M, "us": round(us, 3), "TFLOP_s": round(tf, 2),
                     "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
         log(f"qmm K={c.K} N={c.N}: {us:.3f} us  {tf:.2f} TFLOP/s")
+    # A decoder layer's linears (Llama-3.1-8B shapes, b=4, g=64, M=1): seven
+    # separate launches vs four launches with the multi-linear entry point.
+    lbytes = layer_bytes()
+    L = prepare_layer(max(2, -(-ROTATE_BYTES // lbytes)), dev)
+    torch.cuda.synchronize()
+    n = L["copies"]
+    sep_us = time_graph(capture(lambda i, s: layer_separate(L, i, s), n, stream),
+                        max(2, args.reps // n + 1), n, stream)
+    fus_us = time_graph(capture(lambda i, s: layer_fused(L, i, s), n, stream),
+                        max(2, args.reps // n + 1), n, stream)
+    del L
+    log(f"decoder layer linears: {sep_us:.2f} us as 7 launches, {fus_us:.2f} us as 4")
+    decode_layer = {
+        "model": "Llama-3.1-8B decoder layer linears (q,k,v,o,gate,up,down), M=1, bits 4, group 64, "
+                 "fp16; synthetic weights; attention, norms and activations not included",
+        "bytes": lbytes,
+        "separate_us": round(sep_us, 3), "separate_launches": 7,
+        "fused_us": round(fus_us, 3), "fused_launches": 4,
+        "fused_GB_s": round(lbytes / (fus_us * 1e-6) / 1e9, 1),
+        "linear_only_us_per_token_32_layers": round(32 * fus_us, 2),
+    }
+
     fresh = kernel_source_hash() == MEASURED_TRAFFIC["src_hash"]
     qmv_traffic = MEASURED_TRAFFIC["qmv_bits1to7_bytes"] if fresh else None
     qmm_traffic = (sum(MEASURED_TRAFFIC["qmm_bytes"].values()) if fresh else None)
@@ -324,6 +400,7 @@ def main():
         },
         "qmm": qmm,
         "qmv_eager_us_per_call": [round(u, 3) for u in eager_us],
+        "decode_layer": decode_layer,
         "timing": "per-kernel us = HIP-event time of replays of a HIP graph of back-to-back "
                   "launches (rotating weight copies) / launches; steps replay one graph per "
                   "step; qmv_eager_us_per_call = one Python call per launch (host-bound)",

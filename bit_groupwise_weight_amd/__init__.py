@@ -5,4 +5,4 @@ include/lowbit.h); `lowbit` is its Python binding.  Importing this package does
 not load the library; the first call through `lowbit` does, and raises if the
 library is not built.
 """
-__all__ = ["lowbit", "workloads"]
+__all__ = ["lowbit", "nn", "workloads"]

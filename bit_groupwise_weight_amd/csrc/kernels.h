@@ -45,18 +45,26 @@ struct QmvParams {
 constexpr int qmv_rows_per_group(int bits, int mt) {
   return (mt == 1 && (bits <= 3 || bits == 5)) ? 2 : 1;
 }
+// Up to kQmvMaxProblems decode problems of one bit width, group size and
+// activation dtype served by one launch: blocks with blockIdx.z == i work on
+// problem i (grid.x is sized for the largest; blocks past a problem's rows
+// exit at once); all share M (grid.y).
+constexpr int kQmvMaxProblems = 8;
+struct QmvBatch {
+  QmvParams prob[kQmvMaxProblems];
+};
 struct QmvLaunch {
   dim3 grid, block;
   int mt;                 // activation rows per pass: 1, 2 or 4
 };
 // One entry point per bit width (compiled as separate objects).
-hipError_t launch_qmv_b1(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
-hipError_t launch_qmv_b2(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
-hipError_t launch_qmv_b3(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
-hipError_t launch_qmv_b4(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
-hipError_t launch_qmv_b5(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
-hipError_t launch_qmv_b6(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
-hipError_t launch_qmv_b7(const QmvParams&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b1(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b2(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b3(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b4(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b5(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b6(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
+hipError_t launch_qmv_b7(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
 // LDS bytes the decode kernel stages per activation row and per unit of a round.
 int qmv_stage_bytes_b1(int act);
 int qmv_stage_bytes_b2(int act);

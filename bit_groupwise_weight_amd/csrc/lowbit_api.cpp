@@ -59,6 +59,24 @@ lowbit_status check_common(int bits, int group, int64_t N, int64_t K) {
   return LOWBIT_OK;
 }
 
+// Arguments of one linear (shared by lowbit_linear_path and lowbit_linear_multi).
+lowbit_status check_linear(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                           const void* scales, const void* zeros, const void* bias, const void* y,
+                           int bits, int group, int64_t M, int64_t N, int64_t K) {
+  lowbit_status st = check_common(bits, group, N, K);
+  if (st != LOWBIT_OK) return st;
+  if (M < 0 || M > kMaxDim) return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld", (long long)M);
+  if (!valid_dtype(act_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "act_dtype=%d", (int)act_dtype);
+  if (!packed || !scales || !zeros) return fail(LOWBIT_ERR_INVALID_ARG, "NULL weight pointer");
+  if (M > 0 && (!x || !y)) return fail(LOWBIT_ERR_INVALID_ARG, "NULL x or y");
+  if (!aligned(packed, 16)) return fail(LOWBIT_ERR_MISALIGNED, "packed must be 16-byte aligned");
+  if (!aligned(x, 16)) return fail(LOWBIT_ERR_MISALIGNED, "x must be 16-byte aligned");
+  const size_t e = dtype_bytes(act_dtype);
+  if (!aligned(scales, e) || !aligned(zeros, e) || !aligned(y, e) || (bias && !aligned(bias, e)))
+    return fail(LOWBIT_ERR_MISALIGNED, "scales/zeros/bias/y must be aligned to their element size");
+  return LOWBIT_OK;
+}
+
 // One status word pair per device for lowbit_quantize_pack, allocated on first
 // use and kept for the life of the process.
 constexpr int kMaxDevices = 64;
@@ -89,7 +107,7 @@ int act_kind(lowbit_dtype d) {
   }
 }
 
-typedef hipError_t (*QmvLauncher)(const lowbit::QmvParams&, const lowbit::QmvLaunch&, int, int,
+typedef hipError_t (*QmvLauncher)(const lowbit::QmvBatch&, const lowbit::QmvLaunch&, int, int,
                                   hipStream_t);
 const QmvLauncher kQmv[8] = {nullptr,
                              lowbit::launch_qmv_b1,
@@ -101,6 +119,7 @@ const QmvLauncher kQmv[8] = {nullptr,
                              lowbit::launch_qmv_b7};
 
 constexpr int64_t kQmmMinM = 16;
+static_assert(LOWBIT_MAX_MULTI <= lowbit::kQmvMaxProblems, "one launch serves every desc");
 
 typedef int (*QmvStageBytes)(int);
 const QmvStageBytes kQmvStage[8] = {nullptr,
@@ -134,52 +153,85 @@ int device_cus() {
   return cus;
 }
 
-lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
-                      const void* zeros, const void* bias, void* y, int bits, int group,
-                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  lowbit::QmvParams p{};
-  p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
-  p.M = static_cast<int>(M);
-  p.N = static_cast<int>(N);
-  p.K = static_cast<int>(K);
-  p.units = static_cast<int>((K + 127) / 128);
-  p.groups = static_cast<int>(K / group);
-  p.row_bytes = K * bits / 8;
-  p.aligned16 = (p.row_bytes % 16) == 0;
-  p.sz_vec = (K % 128) == 0;
-  int shift = 0;
-  while ((1 << shift) < p.units && shift < 6) ++shift;
-  p.lpr_shift = shift;
-  const int lanes = 1 << shift;
+// One decode problem of a (possibly multi-problem) launch.
+struct QmvProblem {
+  const void* x;
+  const uint8_t* packed;
+  const void* scales;
+  const void* zeros;
+  const void* bias;
+  void* y;
+  int64_t N, K;
+};
+
+// All problems share bits, group, activation dtype and M; one launch serves
+// them all (blocks are dealt out to the problems in order).
+lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act, int bits, int group,
+                            int64_t M, hipStream_t stream) {
+  lowbit::QmvBatch b{};
+  int max_shift = 0;
+  int64_t max_per_row = 0;
+  for (int i = 0; i < count; ++i) {
+    const QmvProblem& q = probs[i];
+    lowbit::QmvParams& p = b.prob[i];
+    p.x = q.x; p.packed = q.packed; p.scales = q.scales; p.zeros = q.zeros; p.bias = q.bias; p.y = q.y;
+    p.M = static_cast<int>(M);
+    p.N = static_cast<int>(q.N);
+    p.K = static_cast<int>(q.K);
+    p.units = static_cast<int>((q.K + 127) / 128);
+    p.groups = static_cast<int>(q.K / group);
+    p.row_bytes = q.K * bits / 8;
+    p.aligned16 = (p.row_bytes % 16) == 0;
+    p.sz_vec = (q.K % 128) == 0;
+    int shift = 0;
+    while ((1 << shift) < p.units && shift < 6) ++shift;
+    p.lpr_shift = shift;
+    max_shift = std::max(max_shift, shift);
+    max_per_row = std::max<int64_t>(max_per_row,
+                                    static_cast<int64_t>(kQmvStage[bits](act_kind(act))) << shift);
+  }
 
   // Activation rows per pass: as many as fit the LDS stage (at most 4).
   lowbit::QmvLaunch l{};
-  const int64_t per_row = static_cast<int64_t>(kQmvStage[bits](act_kind(act))) * lanes;
   l.mt = 1;
-  if (M >= 2 && 2 * per_row <= kQmvStageBudget) l.mt = 2;
-  if (M >= 3 && 4 * per_row <= kQmvStageBudget) l.mt = 4;
-  if (per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
+  if (M >= 2 && 2 * max_per_row <= kQmvStageBudget) l.mt = 2;
+  if (M >= 3 && 4 * max_per_row <= kQmvStageBudget) l.mt = 4;
+  if (max_per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
   const int R = lowbit::qmv_rows_per_group(bits, l.mt);
 
   // Block size: 256 threads unless that leaves fewer blocks than CUs.
   int threads = env_int("LOWBIT_QMV_BLOCK", 0);
-  auto blocks_for = [&](int t) {
-    const int64_t rows_per_block = static_cast<int64_t>(t >> shift) * R;
-    return (N + rows_per_block - 1) / rows_per_block;
+  auto blocks_for = [&](int t, int i) {
+    const int64_t rows_per_block = static_cast<int64_t>(t >> b.prob[i].lpr_shift) * R;
+    return (probs[i].N + rows_per_block - 1) / rows_per_block;
+  };
+  auto total_blocks = [&](int t) {
+    int64_t n = 0;
+    for (int i = 0; i < count; ++i) n += blocks_for(t, i);
+    return n;
   };
   if (threads != 64 && threads != 128 && threads != 256) {
     threads = 256;
-    while (threads > 64 && blocks_for(threads) < device_cus() && (threads >> 1) >= lanes) threads >>= 1;
+    while (threads > 64 && total_blocks(threads) < device_cus() && (threads >> 1) >= (1 << max_shift))
+      threads >>= 1;
   }
-  if (threads < lanes) threads = lanes;
-  const int64_t bx = blocks_for(threads);
+  if (threads < (1 << max_shift)) threads = 1 << max_shift;
+  int64_t bx = 0;
+  for (int i = 0; i < count; ++i) bx = std::max<int64_t>(bx, blocks_for(threads, i));
   const int64_t by = (M + l.mt - 1) / l.mt;
   if (bx > 0x7fffffff || by > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "problem too large");
-  l.grid = dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by));
+  l.grid = dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by), static_cast<unsigned>(count));
   l.block = dim3(threads);
-  hipError_t e = kQmv[bits](p, l, group, act_kind(act), stream);
+  hipError_t e = kQmv[bits](b, l, group, act_kind(act), stream);
   if (e != hipSuccess) return hip_fail(e, "qmv launch");
   return LOWBIT_OK;
+}
+
+lowbit_status run_qmv(const void* x, lowbit_dtype act, const uint8_t* packed, const void* scales,
+                      const void* zeros, const void* bias, void* y, int bits, int group,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const QmvProblem q{x, packed, scales, zeros, bias, y, N, K};
+  return run_qmv_multi(&q, 1, act, bits, group, M, stream);
 }
 
 typedef hipError_t (*QmmLauncher)(const lowbit::QmmParams&, const lowbit::QmmLaunch&, int,
@@ -340,23 +392,14 @@ lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const ui
                                  void* workspace, size_t workspace_bytes, lowbit_path path,
                                  void* stream) {
   g_last_error.clear();
-  lowbit_status st = check_common(bits, group, N, K);
+  lowbit_status st = check_linear(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K);
   if (st != LOWBIT_OK) return st;
-  if (M < 0 || M > kMaxDim) return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld", (long long)M);
-  if (!valid_dtype(act_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "act_dtype=%d", (int)act_dtype);
   if (path != LOWBIT_PATH_AUTO && path != LOWBIT_PATH_QMV && path != LOWBIT_PATH_QMM)
     return fail(LOWBIT_ERR_INVALID_ARG, "path=%d", (int)path);
   if (workspace == nullptr && workspace_bytes != 0)
     return fail(LOWBIT_ERR_WORKSPACE, "workspace_bytes > 0 with a NULL workspace");
   if (workspace != nullptr && !aligned(workspace, 256))
     return fail(LOWBIT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (!packed || !scales || !zeros) return fail(LOWBIT_ERR_INVALID_ARG, "NULL weight pointer");
-  if (M > 0 && (!x || !y)) return fail(LOWBIT_ERR_INVALID_ARG, "NULL x or y");
-  if (!aligned(packed, 16)) return fail(LOWBIT_ERR_MISALIGNED, "packed must be 16-byte aligned");
-  if (!aligned(x, 16)) return fail(LOWBIT_ERR_MISALIGNED, "x must be 16-byte aligned");
-  const size_t e = dtype_bytes(act_dtype);
-  if (!aligned(scales, e) || !aligned(zeros, e) || !aligned(y, e) || (bias && !aligned(bias, e)))
-    return fail(LOWBIT_ERR_MISALIGNED, "scales/zeros/bias/y must be aligned to their element size");
   if (path == LOWBIT_PATH_QMM && act_dtype == LOWBIT_F32)
     return fail(LOWBIT_ERR_UNSUPPORTED, "the MFMA path takes fp16 or bf16 activations");
   if (M == 0) return LOWBIT_OK;
@@ -379,6 +422,27 @@ lowbit_status lowbit_linear(const void* x, lowbit_dtype act_dtype, const uint8_t
                             size_t workspace_bytes, void* stream) {
   return lowbit_linear_path(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K,
                             workspace, workspace_bytes, LOWBIT_PATH_AUTO, stream);
+}
+
+lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lowbit_dtype act_dtype,
+                                  int bits, int group, int64_t M, void* stream) {
+  g_last_error.clear();
+  if (count < 0 || count > LOWBIT_MAX_MULTI)
+    return fail(LOWBIT_ERR_INVALID_ARG, "count=%d not in 0..%d", count, LOWBIT_MAX_MULTI);
+  if (count > 0 && descs == nullptr) return fail(LOWBIT_ERR_INVALID_ARG, "NULL descs");
+  QmvProblem probs[LOWBIT_MAX_MULTI];
+  for (int i = 0; i < count; ++i) {
+    const lowbit_linear_desc& d = descs[i];
+    const lowbit_status st = check_linear(d.x, act_dtype, d.packed, d.scales, d.zeros, d.bias, d.y,
+                                          bits, group, M, d.N, d.K);
+    if (st != LOWBIT_OK) {
+      const std::string detail = g_last_error;
+      return fail(st, "desc %d: %s", i, detail.c_str());
+    }
+    probs[i] = QmvProblem{d.x, d.packed, d.scales, d.zeros, d.bias, d.y, d.N, d.K};
+  }
+  if (count == 0 || M == 0) return LOWBIT_OK;
+  return run_qmv_multi(probs, count, act_dtype, bits, group, M, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

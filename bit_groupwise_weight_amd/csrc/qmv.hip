@@ -204,8 +204,7 @@ __device__ __forceinline__ void load_raw_run(const void* x, int64_t off,
 // accumulates, per run, P = sum x*q against activations staged in LDS in the
 // form its bit width needs, then y += s*P + z*X (X = sum of the run's x).
 template <int BITS, int GROUP, int ACT, int MT>
-__global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
-  extern __shared__ uint4 stage[];
+__device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint4* stage) {
   constexpr int R = qmv_rows_per_group(BITS, MT);   // rows per row group
   constexpr int RAW = RawWords<ACT>::n;
   constexpr int QD = RunQuads<ACT, BITS>::n;    // staged quads per run
@@ -216,12 +215,12 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   const int lane = tid & (lanes - 1);
   const int rg = tid >> p.lpr_shift;
   const int rgs = blockDim.x >> p.lpr_shift;
-  const int n_base = (blockIdx.x * rgs + rg) * R;
+  const int n_base = (bx * rgs + rg) * R;
   const int m0 = blockIdx.y * MT;
   const int mcount = min(MT, p.M - m0);
   const int nruns = MT * 4 * lanes;              // staged runs per round
   const int runs = p.K >> 5;                     // 32-code runs per row
-  const int rounds = (runs + 4 * lanes - 1) / (4 * lanes);
+  const int rounds = (runs + 4 * lanes - 1) >> (p.lpr_shift + 2);
 
   float acc[R][MT];
 #pragma unroll
@@ -234,8 +233,8 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
     // -- activation loads for this thread's first staged run (issued first).
     // Staged run rr: activation row m, slot j, lane-in-group ul.
     auto run_coords = [&](int rr, int& m, int& ul, int& j) {
-      m = rr / (4 * lanes);
-      const int rem = rr - m * 4 * lanes;
+      m = rr >> (p.lpr_shift + 2);
+      const int rem = rr - (m << (p.lpr_shift + 2));
       ul = rem & (lanes - 1);
       j = rem >> p.lpr_shift;
     };
@@ -249,6 +248,9 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
     };
     uint32_t raw[RAW];
     const bool raw_valid = run_load(tid, raw);
+    // keep the activation loads ahead of the weight loads: staging then waits
+    // only for them, while the weights are still in flight
+    __builtin_amdgcn_sched_barrier(0);
 
     // -- weights, scales and zeros of this lane's four runs (addresses
     // clamped to the matrix; rows past N and runs past K get zero scale and
@@ -349,17 +351,41 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   }
 }
 
+// One problem per launch (its parameters at fixed kernel-argument offsets).
+template <int BITS, int GROUP, int ACT, int MT>
+__global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
+  extern __shared__ uint4 stage[];
+  qmv_block<BITS, GROUP, ACT, MT>(p, static_cast<int>(blockIdx.x), stage);
+}
+
+// Several problems per launch: blockIdx.z selects the problem (no memory
+// access needed to find it); blocks past that problem's rows exit at once.
+template <int BITS, int GROUP, int ACT, int MT>
+__global__ __launch_bounds__(256) void qmv_multi_kernel(QmvBatch b) {
+  extern __shared__ uint4 stage[];
+  const QmvParams& p = b.prob[blockIdx.z];
+  const int rows_per_block = (static_cast<int>(blockDim.x) >> p.lpr_shift) * qmv_rows_per_group(BITS, MT);
+  if (static_cast<int>(blockIdx.x) * rows_per_block >= p.N) return;   // block-uniform
+  qmv_block<BITS, GROUP, ACT, MT>(p, static_cast<int>(blockIdx.x), stage);
+}
+
 template <int GROUP, int ACT, int MT>
-static hipError_t launch_one(const QmvParams& p, const QmvLaunch& l, hipStream_t s) {
-  // staged runs plus one scratch run for threads without a run
-  const size_t lds = (static_cast<size_t>(MT) * 4 * (size_t(1) << p.lpr_shift) + 1) *
+static hipError_t launch_one(const QmvBatch& b, const QmvLaunch& l, hipStream_t s) {
+  // staged runs (sized for the widest lane group) plus one scratch run for
+  // threads without a run
+  int shift = 0;
+  for (unsigned i = 0; i < l.grid.z; ++i) shift = b.prob[i].lpr_shift > shift ? b.prob[i].lpr_shift : shift;
+  const size_t lds = (static_cast<size_t>(MT) * 4 * (size_t(1) << shift) + 1) *
                      RunQuads<ACT, LOWBIT_BITS>::n * 16;
-  qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT><<<l.grid, l.block, lds, s>>>(p);
+  if (l.grid.z == 1)
+    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT><<<l.grid, l.block, lds, s>>>(b.prob[0]);
+  else
+    qmv_multi_kernel<LOWBIT_BITS, GROUP, ACT, MT><<<l.grid, l.block, lds, s>>>(b);
   return hipGetLastError();
 }
 
 template <int GROUP, int ACT>
-static hipError_t dispatch_mt(const QmvParams& p, const QmvLaunch& l, hipStream_t s) {
+static hipError_t dispatch_mt(const QmvBatch& p, const QmvLaunch& l, hipStream_t s) {
   switch (l.mt) {
     case 1: return launch_one<GROUP, ACT, 1>(p, l, s);
     case 2: return launch_one<GROUP, ACT, 2>(p, l, s);
@@ -369,7 +395,7 @@ static hipError_t dispatch_mt(const QmvParams& p, const QmvLaunch& l, hipStream_
 }
 
 template <int GROUP>
-static hipError_t dispatch_act(const QmvParams& p, const QmvLaunch& l, int act, hipStream_t s) {
+static hipError_t dispatch_act(const QmvBatch& p, const QmvLaunch& l, int act, hipStream_t s) {
   switch (act) {
     case ACT_F32: return dispatch_mt<GROUP, ACT_F32>(p, l, s);
     case ACT_F16: return dispatch_mt<GROUP, ACT_F16>(p, l, s);
@@ -380,7 +406,7 @@ static hipError_t dispatch_act(const QmvParams& p, const QmvLaunch& l, int act, 
 
 #define LOWBIT_CAT2(a, b) a##b
 #define LOWBIT_CAT(a, b) LOWBIT_CAT2(a, b)
-hipError_t LOWBIT_CAT(launch_qmv_b, LOWBIT_BITS)(const QmvParams& p, const QmvLaunch& l,
+hipError_t LOWBIT_CAT(launch_qmv_b, LOWBIT_BITS)(const QmvBatch& p, const QmvLaunch& l,
                                                  int group, int act, hipStream_t s) {
   switch (group) {
     case 32: return dispatch_act<32>(p, l, act, s);

@@ -30,9 +30,17 @@ _ENUM_DTYPE = {v: k for k, v in _DTYPE_ENUM.items()}
 
 EXPORTED_SYMBOLS = (
     "lowbit_abi_version", "lowbit_packed_bytes", "lowbit_num_groups", "lowbit_quantize_pack",
-    "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path",
+    "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path", "lowbit_linear_multi",
     "lowbit_status_string", "lowbit_last_error",
 )
+MAX_MULTI = 8   # LOWBIT_MAX_MULTI
+
+
+class LinearDesc(ctypes.Structure):
+    """struct lowbit_linear_desc"""
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class LowbitError(RuntimeError):
@@ -78,6 +86,9 @@ def load() -> ctypes.CDLL:
     lib.lowbit_linear.argtypes = lin + [vp]
     lib.lowbit_linear_path.restype = ctypes.c_int
     lib.lowbit_linear_path.argtypes = lin + [ctypes.c_int, vp]
+    lib.lowbit_linear_multi.restype = ctypes.c_int
+    lib.lowbit_linear_multi.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, c_i64, vp]
     lib.lowbit_status_string.restype = ctypes.c_char_p
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_last_error.restype = ctypes.c_char_p
@@ -219,3 +230,31 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
         st = lib.lowbit_linear_path(*args, int(path), s)
         _check(st, "lowbit_linear_path")
     return y
+
+
+def lowbit_linear_multi(items, bits: int, group: int, stream=None):
+    """Several linears in one launch: items are (x, packed, scales, zeros, bias, y)
+    tuples sharing bits, group, x's dtype and M; y may be None (allocated).
+    Returns the list of outputs."""
+    lib = load()
+    if not items:
+        return []
+    if len(items) > MAX_MULTI:
+        raise ValueError(f"at most {MAX_MULTI} linears per call")
+    x0 = items[0][0]
+    M, dtype = x0.shape[0], x0.dtype
+    descs = (LinearDesc * len(items))()
+    outs = []
+    for i, (x, packed, scales, zeros, bias, y) in enumerate(items):
+        if x.dim() != 2 or x.shape[0] != M or x.dtype != dtype:
+            raise ValueError("every x must be 2-D with the same M and dtype")
+        N, K = scales.shape[0], x.shape[1]
+        if y is None:
+            y = torch.empty((M, N), dtype=dtype, device=x.device)
+        _require_cuda(x, packed, scales, zeros, bias, y)
+        descs[i] = LinearDesc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(bias), _ptr(y), N, K)
+        outs.append(y)
+    st = lib.lowbit_linear_multi(descs, len(items), _DTYPE_ENUM[dtype], bits, group, M,
+                                 _stream_handle(x0.device, stream))
+    _check(st, "lowbit_linear_multi")
+    return outs

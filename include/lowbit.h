@@ -151,6 +151,40 @@ lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const ui
                                  void* workspace, size_t workspace_bytes, lowbit_path path,
                                  void* stream);
 
+/* One linear of a lowbit_linear_multi call (pointers as in lowbit_linear). */
+typedef struct lowbit_linear_desc {
+  const void* x;          /* device, M x K row-major, act_dtype */
+  const uint8_t* packed;  /* device, N x (K*bits/8) bytes, 16-byte aligned */
+  const void* scales;     /* device, N x (K/group), act_dtype */
+  const void* zeros;      /* device, N x (K/group), act_dtype */
+  const void* bias;       /* device, N elements, or NULL */
+  void* y;                /* device, M x N row-major, act_dtype; overwritten */
+  int64_t N;
+  int64_t K;
+} lowbit_linear_desc;
+
+#define LOWBIT_MAX_MULTI 8
+
+/* Several independent linears of one bit width, group size, activation
+ * dtype and M, computed by the decode kernel in ONE launch: the fused
+ * decode step of a layer, e.g. the query/key/value projections or the gate
+ * and up projections, which read the same x (the pages' "metal lowbit
+ * kernels: qmv_fast optimization" measures whole-model decode, where every
+ * linear of a token pays the launch and ramp-up cost; one launch amortizes
+ * it).  Each desc has its own x, weights, bias, y, N and K; x may be shared.
+ * No y may alias any input of any desc.
+ *
+ *   count    1 .. LOWBIT_MAX_MULTI (0 is a no-op that returns LOWBIT_OK).
+ *   M >= 0   rows of every x (M == 0 is a no-op).  Any M is accepted; the
+ *            decode kernel is the one lowbit_linear uses for M < 16.
+ *
+ * Every desc is validated as lowbit_linear validates its arguments before
+ * anything is launched; on an error nothing is written.  Results are
+ * bitwise identical to lowbit_linear_path(..., LOWBIT_PATH_QMV, ...) called
+ * on each desc.  Enqueued on `stream`; asynchronous. */
+lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lowbit_dtype act_dtype,
+                                  int bits, int group, int64_t M, void* stream);
+
 /* Static text for a status code. */
 const char* lowbit_status_string(lowbit_status status);
 

@@ -68,6 +68,40 @@ def test_linear_validation(lowbit_lib, kw, status):
         assert lb.lowbit_last_error() != ""
 
 
+def multi(lib, descs_kw, count=None, **kw):
+    a = dict(act=F16, bits=4, group=64, M=1)
+    a.update(kw)
+    descs = (lb.LinearDesc * max(1, len(descs_kw)))()
+    for i, d in enumerate(descs_kw):
+        v = dict(x=A, packed=A, scales=A, zeros=A, bias=None, y=A, N=64, K=256)
+        v.update(d)
+        descs[i] = lb.LinearDesc(v["x"], v["packed"], v["scales"], v["zeros"], v["bias"], v["y"],
+                                 v["N"], v["K"])
+    n = len(descs_kw) if count is None else count
+    return lib.lowbit_linear_multi(descs, n, a["act"], a["bits"], a["group"], a["M"], None)
+
+
+@pytest.mark.parametrize("descs,kw,status", [
+    ([{}], dict(M=0), OK),                                   # M == 0: no launch
+    ([], dict(), OK),                                        # count == 0: no launch
+    ([{}, {}], dict(M=0), OK),
+    ([{}] * 9, dict(M=0), INVALID),                          # more than LOWBIT_MAX_MULTI
+    ([{}], dict(M=0, bits=8), INVALID),
+    ([{}, dict(K=96)], dict(M=0), INVALID),                  # K % group != 0 in desc 1
+    ([{}, dict(packed=A + 8)], dict(M=0), MISALIGNED),
+    ([dict(y=None)], dict(M=1), INVALID),
+    ([{}], dict(M=0, act=9), UNSUPPORTED),
+])
+def test_multi_validation(lowbit_lib, descs, kw, status):
+    assert multi(lowbit_lib, descs, **kw) == status
+    if status != OK:
+        assert lb.lowbit_last_error() != ""
+
+
+def test_multi_negative_count(lowbit_lib):
+    assert multi(lowbit_lib, [{}], count=-1, M=0) == INVALID
+
+
 def test_qmm_path_rejects_fp32(lowbit_lib):
     st = lowbit_lib.lowbit_linear_path(A, F32, A, A, A, None, A, 4, 64, 32, 64, 256, None, 0, 2,
                                        None)
