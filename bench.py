@@ -40,9 +40,9 @@ ROTATE_BYTES = 1 << 30
 # kernel sources whose sha256 prefix is `src_hash`; for any other sources bench
 # reports traffic as null.
 MEASURED_TRAFFIC = {
-    "src_hash": "5e0c99487a5a2132",
-    "qmv_bits1to7_bytes": 67398148,
-    "qmm_bytes": {"4096x14336": 92089237, "14336x4096": 95508337},
+    "src_hash": "bbd49e213929fd55",
+    "qmv_bits1to7_bytes": 67353990,
+    "qmm_bytes": {"4096x14336": 72917743, "14336x4096": 95496510},
 }
 
 
@@ -69,6 +69,9 @@ def parse():
                     help="launches per kernel in the per-kernel timing loops")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-reps", type=int, default=30)
+    ap.add_argument("--no-decode-layer", action="store_true",
+                    help="skip the decoder-layer section (its q-proj launches share the kernel "
+                         "and grid of the b=4 decode case, which a kernel trace would mix up)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -330,24 +333,27 @@ def main():
     # A decoder layer's linears (Llama-3.1-8B shapes, b=4, g=64, M=1): seven
     # separate launches vs four launches with the multi-linear entry point.
     lbytes = layer_bytes()
-    L = prepare_layer(max(2, -(-ROTATE_BYTES // lbytes)), dev)
-    torch.cuda.synchronize()
-    n = L["copies"]
-    sep_us = time_graph(capture(lambda i, s: layer_separate(L, i, s), n, stream),
-                        max(2, args.reps // n + 1), n, stream)
-    fus_us = time_graph(capture(lambda i, s: layer_fused(L, i, s), n, stream),
-                        max(2, args.reps // n + 1), n, stream)
-    del L
-    log(f"decoder layer linears: {sep_us:.2f} us as 7 launches, {fus_us:.2f} us as 4")
-    decode_layer = {
-        "model": "Llama-3.1-8B decoder layer linears (q,k,v,o,gate,up,down), M=1, bits 4, group 64, "
-                 "fp16; synthetic weights; attention, norms and activations not included",
-        "bytes": lbytes,
-        "separate_us": round(sep_us, 3), "separate_launches": 7,
-        "fused_us": round(fus_us, 3), "fused_launches": 4,
-        "fused_GB_s": round(lbytes / (fus_us * 1e-6) / 1e9, 1),
-        "linear_only_us_per_token_32_layers": round(32 * fus_us, 2),
-    }
+    decode_layer = None
+    if not args.no_decode_layer:
+        L = prepare_layer(max(2, -(-ROTATE_BYTES // lbytes)), dev)
+        torch.cuda.synchronize()
+        n = L["copies"]
+        sep_us = time_graph(capture(lambda i, s: layer_separate(L, i, s), n, stream),
+                            max(2, args.reps // n + 1), n, stream)
+        fus_us = time_graph(capture(lambda i, s: layer_fused(L, i, s), n, stream),
+                            max(2, args.reps // n + 1), n, stream)
+        del L
+        log(f"decoder layer linears: {sep_us:.2f} us as 7 launches, {fus_us:.2f} us as 4")
+        decode_layer = {
+            "model": "Llama-3.1-8B decoder layer linears (q,k,v,o,gate,up,down), M=1, bits 4, "
+                     "group 64, fp16; synthetic weights; attention, norms and activations not "
+                     "included",
+            "bytes": lbytes,
+            "separate_us": round(sep_us, 3), "separate_launches": 7,
+            "fused_us": round(fus_us, 3), "fused_launches": 4,
+            "fused_GB_s": round(lbytes / (fus_us * 1e-6) / 1e9, 1),
+            "linear_only_us_per_token_32_layers": round(32 * fus_us, 2),
+        }
 
     fresh = kernel_source_hash() == MEASURED_TRAFFIC["src_hash"]
     qmv_traffic = MEASURED_TRAFFIC["qmv_bits1to7_bytes"] if fresh else None

@@ -118,7 +118,11 @@ const QmvLauncher kQmv[8] = {nullptr,
                              lowbit::launch_qmv_b6,
                              lowbit::launch_qmv_b7};
 
-constexpr int64_t kQmmMinM = 16;
+// Largest M that the automatic choice sends to the decode kernel: measured
+// on MI355X at K = N = 4096, group 64, fp16 -- the decode kernel is faster up
+// to M = 8 for 1-2 bit codes, M = 6 for 3-4 bits and M = 4 for 5-7 bits
+// (it re-reads the weights once per four activation rows).
+inline int64_t qmv_max_m(int bits) { return bits <= 2 ? 8 : bits <= 4 ? 6 : 4; }
 static_assert(LOWBIT_MAX_MULTI <= lowbit::kQmvMaxProblems, "one launch serves every desc");
 
 typedef int (*QmvStageBytes)(int);
@@ -407,7 +411,7 @@ lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const ui
   bool use_qmm;
   if (path == LOWBIT_PATH_QMV) use_qmm = false;
   else if (path == LOWBIT_PATH_QMM) use_qmm = true;
-  else use_qmm = (M >= kQmmMinM) && act_dtype != LOWBIT_F32;
+  else use_qmm = (M > qmv_max_m(bits)) && act_dtype != LOWBIT_F32;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_qmm)

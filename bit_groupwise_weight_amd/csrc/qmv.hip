@@ -325,6 +325,14 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
           acc[r][m] = __builtin_fmaf(sv, dq, acc[r][m]);
           acc[r][m] = __builtin_fmaf(zv, X, acc[r][m]);
         }
+        // With several activation rows, keep one staged fragment live at a
+        // time (hoisting them all would take MT*4*QD*4 registers): the empty
+        // asm consumes this fragment's sums and, as a memory clobber, keeps
+        // the next fragment's LDS reads behind them.
+        if constexpr (MT > 1) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[r][m]) : : "memory");
+        }
       }
     }
     if (t + 1 < rounds) __syncthreads();

@@ -74,7 +74,9 @@ typedef enum lowbit_dtype {
 
 /* Which kernel family lowbit_linear_path runs. */
 typedef enum lowbit_path {
-  LOWBIT_PATH_AUTO = 0,  /* qmv for M < 16 or fp32 activations, qmm otherwise */
+  LOWBIT_PATH_AUTO = 0,  /* qmv for fp32 activations and for M <= 8 (1-2 bit
+                            codes), M <= 6 (3-4 bits), M <= 4 (5-7 bits);
+                            qmm otherwise */
   LOWBIT_PATH_QMV = 1,   /* decode matrix-vector kernel, any M              */
   LOWBIT_PATH_QMM = 2    /* MFMA matrix-matrix kernel, fp16/bf16 only       */
 } lowbit_path;
@@ -176,7 +178,7 @@ typedef struct lowbit_linear_desc {
  *
  *   count    1 .. LOWBIT_MAX_MULTI (0 is a no-op that returns LOWBIT_OK).
  *   M >= 0   rows of every x (M == 0 is a no-op).  Any M is accepted; the
- *            decode kernel is the one lowbit_linear uses for M < 16.
+ *            decode kernel is the one lowbit_linear uses for small M.
  *
  * Every desc is validated as lowbit_linear validates its arguments before
  * anything is launched; on an error nothing is written.  Results are
