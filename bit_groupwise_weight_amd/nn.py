@@ -1,13 +1,14 @@
 """torch-facing layer on top of the C ABI: custom ops and a drop-in linear module.
 
-The pages describe a quantize-then-swap flow ("[Feature] Allow for on the
-fly quantization in UIntxWeightOnlyQuantizedLinear", Summary and the code it
-adds): an ``nn.Linear`` is replaced by a module that quantizes its weight
-once, keeps the packed codes and the per-group scales and zeros, and runs the
-low-bit kernel in ``forward``; every bit width 1..7 must be reachable (the
-review thread of that page).  "Add support for fbgemm int4 mm kernel" notes
-that an op without a shape (meta) function cannot be traced by
-``torch.compile``; the ops registered here carry one.
+The issue "Revamp int4 MPS support in torchao" (issue text) asks for a
+module built directly on the weight-only quantized linear that quantizes on
+the fly and accepts a bias, and its thread shows a user broken by one missing
+bit width: here an ``nn.Linear`` is replaced by a module that quantizes its
+weight once, keeps the packed codes and the per-group scales and zeros, and
+runs the low-bit kernel in ``forward``, for every bit width 1..7.  "Add
+support for fbgemm int4 mm kernel" notes that an op without a shape (meta)
+function cannot be traced by ``torch.compile``; the ops registered here carry
+one.
 
 Ops (namespace ``lowbit``):
 
