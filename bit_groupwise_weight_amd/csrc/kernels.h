@@ -90,9 +90,10 @@ struct QmmParams {
   int64_t row_bytes;      // K * bits / 8
 };
 struct QmmLaunch {
-  dim3 grid;              // (ceil(N/(64*nt)), ceil(M/(16*mtt)), k-splits)
+  dim3 grid;              // (ceil(N/(16*nt*waves)), ceil(M/(16*mtt)), k-splits)
   int mtt;                // 16-row MFMA tiles per block: 1, 2, 4 or 8
   int nt;                 // 16-column MFMA tiles per wave: 2 or 4
+  int waves;              // waves per block: 4, or 8 (with nt == 2)
 };
 hipError_t launch_qmm_b1(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b2(const QmmParams&, const QmmLaunch&, int act, hipStream_t);

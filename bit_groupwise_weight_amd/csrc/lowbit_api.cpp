@@ -249,10 +249,10 @@ const QmmLauncher kQmm[8] = {nullptr,
                              lowbit::launch_qmm_b6,
                              lowbit::launch_qmm_b7};
 
-// Schedule of the MFMA kernel: block tile (16*mtt) x 128, K steps of 128,
-// and a K split that brings the grid to about `target` blocks.
+// Schedule of the MFMA kernel: block tile (16*mtt) x (16*nt*waves), K steps
+// of 128, and a K split that fills the CUs with one block each.
 struct QmmSchedule {
-  int mtt, nt;
+  int mtt, nt, waves;
   int64_t tiles_n, tiles_m, ksteps;
   int splits, ksteps_per_split;
   size_t partial_bytes;
@@ -262,7 +262,16 @@ QmmSchedule qmm_schedule(int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   sc.nt = env_int("LOWBIT_QMM_NT", 2) == 4 ? 4 : 2;
-  sc.tiles_n = (N + 64 * sc.nt - 1) / (64 * sc.nt);
+  // Two waves per SIMD (8-wave blocks, 256 columns) for full 128-row tiles
+  // when N is wide enough that the K split stays small: one wave's
+  // dequantization then runs under the other's MFMAs (measured 1.6x more work
+  // per CU than 4-wave blocks at M = 128, K = 4096, N = 14336), but the wider
+  // tile needs twice the K splits, whose partial planes cost more than that
+  // gain once the split exceeds ~4 (N = 4096 is faster with 4-wave blocks).
+  const int wv_default = (sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
+  sc.waves = (sc.nt == 2 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
+  const int64_t bn = 16 * sc.nt * sc.waves;
+  sc.tiles_n = (N + bn - 1) / bn;
   sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
   sc.ksteps = (K + 127) / 128;
   // One block per CU (each block takes a whole CU's register file): split K
@@ -305,6 +314,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   lowbit::QmmLaunch l{};
   l.mtt = sc.mtt;
   l.nt = sc.nt;
+  l.waves = sc.waves;
   l.grid = dim3(static_cast<unsigned>(sc.tiles_n), static_cast<unsigned>(sc.tiles_m),
                 static_cast<unsigned>(sc.splits));
   hipError_t e = kQmm[bits](p, l, act_kind(act), stream);

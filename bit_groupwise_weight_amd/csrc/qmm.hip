@@ -163,11 +163,13 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
-// One block: 16*MTT rows x 64*NT columns, 4 waves; wave w owns columns
-// [16*NT*w, 16*NT*(w+1)) as NT 16-wide MFMA tiles and all rows.  One block
-// per CU: the register budget is the whole SIMD.
-template <int BITS, int ACT, int MTT, int NT>
-__global__ __launch_bounds__(256, 1) void qmm_kernel(QmmParams p) {
+// One block: 16*MTT rows x 16*NT*WV columns, WV waves (4 or 8); wave w owns
+// columns [16*NT*w, 16*NT*(w+1)) as NT 16-wide MFMA tiles and all rows.  One
+// block per CU: with 4 waves each wave has a whole SIMD's registers; with 8,
+// two waves share a SIMD, so one wave's dequantization can run while the
+// other's MFMAs execute.
+template <int BITS, int ACT, int MTT, int NT, int WV>
+__global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
   constexpr int STAGE = MTT * 16 * 16;   // uint4 per activation stage (16*MTT rows x 256 B)
   constexpr int MH = MTT > 1 ? MTT / 2 : 1;   // activation fragments are refilled in two halves
   __shared__ uint4 stage0[STAGE];
@@ -178,7 +180,11 @@ __global__ __launch_bounds__(256, 1) void qmm_kernel(QmmParams p) {
   const int lane = tid & 63;
   const int fr = lane & 15;           // row / column inside a 16-wide MFMA tile
   const int g = lane >> 4;            // lane group: K positions [32g, 32g+32) of a step
-  const int n0 = blockIdx.x * (64 * NT);
+  const int n0 = blockIdx.x * (16 * NT * WV);
+  // activation row quads (4 rows x 256 bytes = one load instruction per wave)
+  // per step, and how many of them each wave loads
+  constexpr int RQ = 4 * MTT;
+  constexpr int XL = (RQ + WV - 1) / WV;
   const int m0 = blockIdx.y * (16 * MTT);
   const int ksteps = (p.K + QMM_BK - 1) / QMM_BK;
   const int s_begin = blockIdx.z * p.ksteps_per_split;
@@ -232,31 +238,33 @@ __global__ __launch_bounds__(256, 1) void qmm_kernel(QmmParams p) {
   // Activation stage: the 16*MTT x 128 tile of one step, rows of 256 bytes
   // (16 chunks of 8 elements) with chunk c of row r stored at position
   // c ^ (r & 15), so that the 16 lanes reading one k-sub of an MFMA tile hit
-  // 16 different 16-byte bank groups.  Load i of wave w covers rows
-  // 4*(4i + w) .. +3: lane l fetches the chunk that belongs at position l & 15
-  // of row 4*(4i + w) + l/16, and later stores it at byte 16 l of those four
-  // rows.  Rows past M and chunks past K read a clamped in-range address: such
+  // 16 different 16-byte bank groups.  Load i of wave w covers row quad
+  // q = WV*i + w (rows 4q .. 4q+3; quads past the tile are skipped): lane l
+  // fetches the chunk that belongs at position l & 15 of row 4q + l/16, and
+  // later stores it at byte 16 l of those four rows.  Rows past M and chunks past K read a clamped in-range address: such
   // a row only feeds output rows that are never stored, and past K the
   // weights are dequantized with s = z = 0.
-  const uint16_t* xrow[MTT];
-  int xchunk[MTT];
+  const uint16_t* xrow[XL];
+  int xchunk[XL];
 #pragma unroll
-  for (int i = 0; i < MTT; ++i) {
-    const int row = 4 * (4 * i + wave) + (lane >> 4);
+  for (int i = 0; i < XL; ++i) {
+    const int row = min(4 * (WV * i + wave), 16 * MTT - 4) + (lane >> 4);
     xchunk[i] = 8 * ((lane & 15) ^ (row & 15));
     xrow[i] = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.K;
   }
   // (native vectors: HIP's uint4 is a struct whose copies become memcpys
   // that keep these arrays out of registers)
-  auto load_x = [&](int step, u32x4_t (&xr)[MTT]) {
+  auto load_x = [&](int step, u32x4_t (&xr)[XL]) {
     const int kb = min(step, s_end - 1) * QMM_BK;
 #pragma unroll
-    for (int i = 0; i < MTT; ++i)
+    for (int i = 0; i < XL; ++i)
       xr[i] = *reinterpret_cast<const u32x4_t*>(xrow[i] + min(kb + xchunk[i], p.K - 8));
   };
-  auto store_x = [&](const u32x4_t (&xr)[MTT], uint4* stage) {
+  auto store_x = [&](const u32x4_t (&xr)[XL], uint4* stage) {
 #pragma unroll
-    for (int i = 0; i < MTT; ++i) reinterpret_cast<u32x4_t*>(stage)[(4 * i + wave) * 64 + lane] = xr[i];
+    for (int i = 0; i < XL; ++i)
+      if (RQ % WV == 0 || WV * i + wave < RQ)    // wave-uniform
+        reinterpret_cast<u32x4_t*>(stage)[(WV * i + wave) * 64 + lane] = xr[i];
   };
 
   float4_t acc[MTT][NT];
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void qmm_kernel(QmmParams p) {
   }
 
   Codes ca, cb;
-  u32x4_t xa[MTT], xb[MTT];
+  u32x4_t xa[XL], xb[XL];
   load_x(s_begin, xa);
   load_x(s_begin + 1, xb);
   load_codes(s_begin, ca);
@@ -454,22 +462,21 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, int splits
 }
 
 template <int ACT, int MTT>
-static hipError_t launch_mtt(const QmmParams& p, int nt, dim3 grid, hipStream_t s) {
-  switch (nt) {
-    case 2: qmm_kernel<LOWBIT_BITS, ACT, MTT, 2><<<grid, dim3(256), 0, s>>>(p); break;
-    case 4: qmm_kernel<LOWBIT_BITS, ACT, MTT, 4><<<grid, dim3(256), 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
-  }
+static hipError_t launch_mtt(const QmmParams& p, int nt, int waves, dim3 grid, hipStream_t s) {
+  if (nt == 2 && waves == 4) qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 4><<<grid, dim3(256), 0, s>>>(p);
+  else if (nt == 4 && waves == 4) qmm_kernel<LOWBIT_BITS, ACT, MTT, 4, 4><<<grid, dim3(256), 0, s>>>(p);
+  else if (nt == 2 && waves == 8) qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 8><<<grid, dim3(512), 0, s>>>(p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <int ACT>
-static hipError_t launch_act(const QmmParams& p, int mtt, int nt, dim3 grid, hipStream_t s) {
+static hipError_t launch_act(const QmmParams& p, int mtt, int nt, int waves, dim3 grid, hipStream_t s) {
   switch (mtt) {
-    case 1: return launch_mtt<ACT, 1>(p, nt, grid, s);
-    case 2: return launch_mtt<ACT, 2>(p, nt, grid, s);
-    case 4: return launch_mtt<ACT, 4>(p, nt, grid, s);
-    case 8: return launch_mtt<ACT, 8>(p, nt, grid, s);
+    case 1: return launch_mtt<ACT, 1>(p, nt, waves, grid, s);
+    case 2: return launch_mtt<ACT, 2>(p, nt, waves, grid, s);
+    case 4: return launch_mtt<ACT, 4>(p, nt, waves, grid, s);
+    case 8: return launch_mtt<ACT, 8>(p, nt, waves, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -480,8 +487,8 @@ hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLa
                                                  hipStream_t s) {
   hipError_t e;
   switch (act) {
-    case ACT_F16: e = launch_act<ACT_F16>(p, l.mtt, l.nt, l.grid, s); break;
-    case ACT_BF16: e = launch_act<ACT_BF16>(p, l.mtt, l.nt, l.grid, s); break;
+    case ACT_F16: e = launch_act<ACT_F16>(p, l.mtt, l.nt, l.waves, l.grid, s); break;
+    case ACT_BF16: e = launch_act<ACT_BF16>(p, l.mtt, l.nt, l.waves, l.grid, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || l.grid.z == 1) return e;
