@@ -4,11 +4,14 @@ Every source is compiled with hipcc for --offload-arch=gfx950 with packed-fp32
 instruction selection disabled.  The quantizer is compiled with
 -ffp-contract=off so that its fp32 steps stay single operations.  The
 decode and MFMA kernels are compiled once per bit width (-DLOWBIT_BITS=b).
+The build fails if any kernel spills registers to scratch memory (read from
+the compiler's kernel resource remarks).
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -44,16 +47,33 @@ def _units():
     return units
 
 
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+_NAME_RE = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH_RE = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
 def _compile(unit):
+    """Compile one unit; returns (diagnostics, {kernel: scratch bytes per lane})."""
     src, obj, extra = unit
-    cmd = [hipcc()] + COMMON_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o",
-                                               os.path.join(BUILD_DIR, obj)]
+    cmd = [hipcc()] + COMMON_FLAGS + extra + RESOURCE_REMARKS + [
+        "-c", os.path.join(CSRC, src), "-o", os.path.join(BUILD_DIR, obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature; that note is harmless.
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    scratch, name = {}, None
+    for line in r.stderr.splitlines():
+        m = _NAME_RE.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SCRATCH_RE.search(line)
+        if m and name:
+            scratch[name] = int(m.group(1))
+    # hipcc's host pass does not know the packed-fp32 feature, and the
+    # resource remarks are collected above; neither is a diagnostic.
+    err = "\n".join(l for l in r.stderr.splitlines()
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src} ({obj}):\n{' '.join(cmd)}\n{err}")
-    return err.strip()
+    return err.strip(), scratch
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
@@ -61,10 +81,17 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     units = _units()
     jobs = jobs or min(len(units), max(1, min(16, os.cpu_count() or 4)))
+    spills = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        for unit, msg in zip(units, ex.map(_compile, units)):
+        for unit, (msg, scratch) in zip(units, ex.map(_compile, units)):
             if msg and verbose:
                 print(f"[{unit[1]}] {msg}", file=sys.stderr)
+            spills.update({k: v for k, v in scratch.items() if v > 0})
+    # A kernel that spills registers to scratch memory runs several times
+    # slower; none of the decode or MFMA kernels may.
+    if spills:
+        listing = "\n".join(f"  {k}: {v} bytes/lane" for k, v in sorted(spills.items()))
+        raise RuntimeError(f"kernels spill registers to scratch memory:\n{listing}")
     objs = [os.path.join(BUILD_DIR, u[1]) for u in units]
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

@@ -31,12 +31,9 @@ struct QmvParams {
   const void* bias;       // N act or nullptr
   void* y;                // M x N act
   int M, N, K;
-  int units;              // ceil(K / 128): 128-code units per row
   int lpr_shift;          // log2(lanes cooperating on one row group), <= 6
   int groups;             // K / group
   int64_t row_bytes;      // K * bits / 8
-  int aligned16;          // row_bytes % 16 == 0 (every row starts 16-byte aligned)
-  int sz_vec;             // K % 128 == 0: a unit's scales/zeros are one aligned vector
 };
 // Rows per row group of the decode kernel for one activation row per pass:
 // two rows for 1, 2, 3 and 5-bit codes, one for 4, 6 and 7 bits (measured on
@@ -89,11 +86,13 @@ struct QmmParams {
   int ksteps_per_split;   // 128-wide K steps per grid.z slice
   int64_t row_bytes;      // K * bits / 8
 };
+// Largest bit width with an 8-wave MFMA kernel instance.
+constexpr int qmm_max_bits_8waves = 5;
 struct QmmLaunch {
   dim3 grid;              // (ceil(N/(16*nt*waves)), ceil(M/(16*mtt)), k-splits)
   int mtt;                // 16-row MFMA tiles per block: 1, 2, 4 or 8
-  int nt;                 // 16-column MFMA tiles per wave: 2 or 4
-  int waves;              // waves per block: 4, or 8 (with nt == 2)
+  int nt;                 // 16-column MFMA tiles per wave (2)
+  int waves;              // waves per block: 4, or 8 (bits <= qmm_max_bits_8waves)
 };
 hipError_t launch_qmm_b1(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b2(const QmmParams&, const QmmLaunch&, int act, hipStream_t);

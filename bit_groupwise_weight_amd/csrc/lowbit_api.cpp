@@ -182,13 +182,12 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
     p.M = static_cast<int>(M);
     p.N = static_cast<int>(q.N);
     p.K = static_cast<int>(q.K);
-    p.units = static_cast<int>((q.K + 127) / 128);
     p.groups = static_cast<int>(q.K / group);
     p.row_bytes = q.K * bits / 8;
-    p.aligned16 = (p.row_bytes % 16) == 0;
-    p.sz_vec = (q.K % 128) == 0;
+    // lanes per row group: enough for four 32-code runs each, at most 64
+    const int64_t units = (q.K + 127) / 128;
     int shift = 0;
-    while ((1 << shift) < p.units && shift < 6) ++shift;
+    while ((int64_t(1) << shift) < units && shift < 6) ++shift;
     p.lpr_shift = shift;
     max_shift = std::max(max_shift, shift);
     max_per_row = std::max<int64_t>(max_per_row,
@@ -258,18 +257,19 @@ struct QmmSchedule {
   size_t partial_bytes;
 };
 
-QmmSchedule qmm_schedule(int64_t M, int64_t N, int64_t K) {
+QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  sc.nt = env_int("LOWBIT_QMM_NT", 2) == 4 ? 4 : 2;
+  sc.nt = 2;
   // Two waves per SIMD (8-wave blocks, 256 columns) for full 128-row tiles
   // when N is wide enough that the K split stays small: one wave's
   // dequantization then runs under the other's MFMAs (measured 1.6x more work
   // per CU than 4-wave blocks at M = 128, K = 4096, N = 14336), but the wider
   // tile needs twice the K splits, whose partial planes cost more than that
   // gain once the split exceeds ~4 (N = 4096 is faster with 4-wave blocks).
-  const int wv_default = (sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
-  sc.waves = (sc.nt == 2 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
+  const bool can8 = bits <= lowbit::qmm_max_bits_8waves;
+  const int wv_default = (can8 && sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
+  sc.waves = (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
   const int64_t bn = 16 * sc.nt * sc.waves;
   sc.tiles_n = (N + bn - 1) / bn;
   sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
@@ -292,7 +292,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
                       const void* zeros, const void* bias, void* y, int bits, int group,
                       int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
-  QmmSchedule sc = qmm_schedule(M, N, K);
+  QmmSchedule sc = qmm_schedule(bits, M, N, K);
   if (sc.splits > 1 && (workspace == nullptr || workspace_bytes < sc.partial_bytes)) {
     sc.splits = 1;                               // no workspace: one block per tile over all K
     sc.ksteps_per_split = static_cast<int>(sc.ksteps);
@@ -396,7 +396,7 @@ size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, 
       M > kMaxDim || N > kMaxDim || K > kMaxDim || !valid_dtype(act_dtype))
     return 0;
   if (act_dtype == LOWBIT_F32) return 0;         // fp32 runs the decode kernel only
-  const QmmSchedule sc = qmm_schedule(M, N, K);
+  const QmmSchedule sc = qmm_schedule(bits, M, N, K);
   return sc.partial_bytes;
 }
 

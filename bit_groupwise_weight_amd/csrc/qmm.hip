@@ -461,12 +461,23 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, int splits
   }
 }
 
+// Instances: 4-wave blocks for every bit width; 8-wave blocks (256 registers
+// per wave) for bit widths up to qmm_max_bits_8waves, above which the code
+// registers of the pipeline no longer fit without spilling.
 template <int ACT, int MTT>
 static hipError_t launch_mtt(const QmmParams& p, int nt, int waves, dim3 grid, hipStream_t s) {
-  if (nt == 2 && waves == 4) qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 4><<<grid, dim3(256), 0, s>>>(p);
-  else if (nt == 4 && waves == 4) qmm_kernel<LOWBIT_BITS, ACT, MTT, 4, 4><<<grid, dim3(256), 0, s>>>(p);
-  else if (nt == 2 && waves == 8) qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 8><<<grid, dim3(512), 0, s>>>(p);
-  else return hipErrorInvalidValue;
+  if (nt != 2) return hipErrorInvalidValue;
+  if (waves == 4) {
+    qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 4><<<grid, dim3(256), 0, s>>>(p);
+  } else if (waves == 8) {
+    if constexpr (LOWBIT_BITS <= qmm_max_bits_8waves) {
+      qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 8><<<grid, dim3(512), 0, s>>>(p);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
