@@ -260,6 +260,8 @@ struct QmmSchedule {
 QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  const int mtt_env = env_int("LOWBIT_QMM_MTT", 0);
+  if (mtt_env == 1 || mtt_env == 2 || mtt_env == 4 || mtt_env == 8) sc.mtt = std::min(sc.mtt, mtt_env);
   sc.nt = 2;
   // Two waves per SIMD (8-wave blocks, 256 columns) for full 128-row tiles
   // when N is wide enough that the K split stays small: one wave's
@@ -269,6 +271,7 @@ QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   // gain once the split exceeds ~4 (N = 4096 is faster with 4-wave blocks).
   const bool can8 = bits <= lowbit::qmm_max_bits_8waves;
   const int wv_default = (can8 && sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
+  // (LOWBIT_QMM_MTT and LOWBIT_QMM_WAVES override the choices for tuning)
   sc.waves = (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
   const int64_t bn = 16 * sc.nt * sc.waves;
   sc.tiles_n = (N + bn - 1) / bn;

@@ -133,6 +133,36 @@ def test_qmm_small(bits, act):
         run_small_linear(M, N, K, bits, group, act, bias, lb.PATH_QMM, seed=bits + M + K)
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("bits", [1, 3, 4, 5, 7])
+def test_qmm_block_variants(bits, waves, monkeypatch):
+    """Both MFMA block shapes (4 waves x 128 columns, 8 waves x 256 columns;
+    8-wave instances exist up to 5 bits, above that the 4-wave kernel runs)
+    on ragged shapes: rows past M, columns past N, a last K step of 32."""
+    monkeypatch.setenv("LOWBIT_QMM_WAVES", waves)
+    for (M, N, K, group, bias) in [(128, 300, 416, 32, True), (100, 520, 1024, 64, False),
+                                   (77, 257, 2080, 32, True)]:
+        run_small_linear(M, N, K, bits, group, "bf16", bias, lb.PATH_QMM, seed=bits + N)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 6])
+def test_qmm_without_workspace(bits):
+    """With too little workspace the MFMA path runs without a K split (one
+    block per tile over all of K)."""
+    case = Case("nows", 96, 1536, 384, bits, 64, "f16", bias=True, seed=bits)
+    W = weight_for(case).numpy()
+    ref = oracle.quantize(W, bits, 64, "f16")
+    x = make_x(case)
+    b = make_bias(case)
+    y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], 64, bias_values(b))
+    packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, "f16")
+    tiny = torch.empty(256, dtype=torch.uint8, device=DEV)       # too small for any split
+    y = lb.lowbit_linear(x.to(DEV), packed, s, z, b.to(DEV), bits, 64, workspace=tiny,
+                         path=lb.PATH_QMM)
+    torch.cuda.synchronize()
+    check_close(y, y_ref, A, f"qmm without workspace b={bits}")
+
+
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [1, 4, 7])
 def test_cross_path_m16(bits, act):
