@@ -62,7 +62,8 @@ hipError_t launch_qmv_b4(const QmvBatch&, const QmvLaunch&, int group, int act, 
 hipError_t launch_qmv_b5(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
 hipError_t launch_qmv_b6(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
 hipError_t launch_qmv_b7(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);
-// LDS bytes the decode kernel stages per activation row and per unit of a round.
+// LDS bytes the decode kernel stages per activation row and per lane of a
+// round (four 32-code runs).
 int qmv_stage_bytes_b1(int act);
 int qmv_stage_bytes_b2(int act);
 int qmv_stage_bytes_b3(int act);

@@ -1,4 +1,4 @@
-// Matrix-matrix kernel (M >= 16): y = x . dequant(Wq)^T (+ bias) on MFMA.
+// Matrix-matrix kernel (M above the decode range): y = x . dequant(Wq)^T (+ bias) on MFMA.
 //
 // The pages ask whether the decode approach of "metal lowbit kernels:
 // qmv_fast optimization" also works for a GEMM (closing review comment), and
@@ -6,8 +6,8 @@
 // int4 weight-only decode falling far behind -- the batched path matters.
 //
 // Layout on CDNA4 (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation):
-//   * block tile: 16*MTT rows (M) x 64*NT columns (N); 4 waves, wave w owns
-//     NT 16-wide column tiles and all M rows; one block per CU;
+//   * block tile: 16*MTT rows (M) x 32*WV columns (N); WV = 4 or 8 waves,
+//     wave w owns two 16-wide column tiles and all M rows; one block per CU;
 //   * K advances in steps of 128.  Within a step, lane group g = lane/16 owns
 //     the 32 consecutive K positions [32g, 32g+32); MFMA slot 8g+t of k-sub
 //     ks (0..3) is K position 32g + 8ks + t for both operands, so each lane's

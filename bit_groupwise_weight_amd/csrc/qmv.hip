@@ -425,7 +425,8 @@ hipError_t LOWBIT_CAT(launch_qmv_b, LOWBIT_BITS)(const QmvBatch& p, const QmvLau
   }
 }
 
-// Staged LDS bytes per activation row and unit of a round (host-side sizing).
+// Staged LDS bytes per activation row and per four-run slot group of a lane
+// in a round (host-side sizing).
 #define LOWBIT_QMV_STAGE(ACTK) (4 * RunQuads<ACTK, LOWBIT_BITS>::n * 16)
 int LOWBIT_CAT(qmv_stage_bytes_b, LOWBIT_BITS)(int act) {
   switch (act) {
