@@ -19,7 +19,7 @@
 //     4-bit codes are split into even / odd byte planes so that each code
 //     converts straight from a byte;
 //   * the activation tile (16*MTT x 128) is shared by the 4 waves through
-//     two LDS stages (XOR-swizzled rows); it is loaded into registers two
+//     two LDS stages (rows swizzled by XOR); it is loaded into registers two
 //     steps ahead and stored into the next stage while the current one is
 //     read;
 //   * codes are loaded two steps ahead; the MFMAs of each k-sub are issued
@@ -140,6 +140,13 @@ __device__ __forceinline__ uint4 dequant_ksub(const uint32_t (&w)[BITS], float s
   }
 }
 
+// LDS swizzle of the activation stage: chunk c of row r sits at position
+// c ^ stage_swizzle(r & 15), the 4-bit row index rotated by two bits.  A
+// k-sub read of an MFMA tile (16 rows, 4 lane groups of 16 lanes) then runs at
+// ~200 B/clk per CU on gfx950; the plain c ^ (r & 15) measured 120 B/clk
+// (contiguous reads: 234).
+__device__ __forceinline__ int stage_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Pair J (codes 8KS+2J and 8KS+2J+1) of k-sub KS of a 32-code run, packed
 // into one operand dword.  For 4-bit codes, lo / hi are the byte planes of
 // word KS (even codes, odd codes), so every code converts straight from a byte.
@@ -237,8 +244,7 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
 
   // Activation stage: the 16*MTT x 128 tile of one step, rows of 256 bytes
   // (16 chunks of 8 elements) with chunk c of row r stored at position
-  // c ^ (r & 15), so that the 16 lanes reading one k-sub of an MFMA tile hit
-  // 16 different 16-byte bank groups.  Load i of wave w covers row quad
+  // c ^ stage_swizzle(r & 15) (see there).  Load i of wave w covers row quad
   // q = WV*i + w (rows 4q .. 4q+3; quads past the tile are skipped): lane l
   // fetches the chunk that belongs at position l & 15 of row 4q + l/16, and
   // later stores it at byte 16 l of those four rows.  Rows past M and chunks past K read a clamped in-range address: such
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
 #pragma unroll
   for (int i = 0; i < XL; ++i) {
     const int row = min(4 * (WV * i + wave), 16 * MTT - 4) + (lane >> 4);
-    xchunk[i] = 8 * ((lane & 15) ^ (row & 15));
+    xchunk[i] = 8 * ((lane & 15) ^ stage_swizzle(row & 15));
     xrow[i] = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.K;
   }
   // (native vectors: HIP's uint4 is a struct whose copies become memcpys
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
     constexpr int KS = decltype(KSc)::value;
     static_for<decltype(MT1c)::value - decltype(MT0c)::value>([&](auto ic) {
       constexpr int mt = decltype(MT0c)::value + decltype(ic)::value;
-      af[mt] = stage[(16 * mt + fr) * 16 + ((4 * g + KS) ^ fr)];
+      af[mt] = stage[(16 * mt + fr) * 16 + ((4 * g + KS) ^ stage_swizzle(fr))];
     });
   };
   using I0 = std::integral_constant<int, 0>;
