@@ -34,15 +34,18 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 ROTATE_BYTES = 1 << 30
 
-# HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes whose
-# commands and scaling are recorded in profiles/ (FETCH_SIZE x 1.9997,
-# WRITE_SIZE x 1.0000, from a plain 256 MiB copy).  They describe the
+# HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes (and
+# the MFMA kernel's MfmaUtil) whose commands and scaling are recorded in
+# profiles/ (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0000, from a plain 256 MiB
+# copy).  They describe the
 # kernel sources whose sha256 prefix is `src_hash`; for any other sources bench
 # reports traffic as null.
 MEASURED_TRAFFIC = {
-    "src_hash": "bbd49e213929fd55",
-    "qmv_bits1to7_bytes": 67353990,
-    "qmm_bytes": {"4096x14336": 72917743, "14336x4096": 95496510},
+    "src_hash": "30a9a51043a19155",
+    "qmv_bits1to7_bytes": 67358406,
+    "qmm_bytes": {"4096x14336": 116805529, "14336x4096": 95493394},
+    # rocprofv3 MfmaUtil (%) of the main MFMA kernel per shape
+    "qmm_mfma_util": {"4096x14336": 17.33, "14336x4096": 16.06},
 }
 
 
@@ -358,6 +361,7 @@ def main():
     fresh = kernel_source_hash() == MEASURED_TRAFFIC["src_hash"]
     qmv_traffic = MEASURED_TRAFFIC["qmv_bits1to7_bytes"] if fresh else None
     qmm_traffic = (sum(MEASURED_TRAFFIC["qmm_bytes"].values()) if fresh else None)
+    qmm_util = MEASURED_TRAFFIC["qmm_mfma_util"] if fresh else None
     qmm_fl = sum(2.0 * c.M * c.N * c.K for c in mcases)
     qmm_tf = qmm_fl / (sum(qmm_us) * 1e-6) / 1e12
 
@@ -403,6 +407,9 @@ def main():
             "traffic": qmm_traffic,
             "traffic_note": "HBM bytes of the two shapes' launches incl. the split-K reduce "
                             "(rocprofv3, scaled); algorithmic bytes: " + str(qmm_bytes_all),
+            "mfma_util_pct": qmm_util,
+            "mfma_util_note": "rocprofv3 MfmaUtil of the main kernel per (K x N) shape, from the "
+                              "profile of the same kernel sources; null for other sources",
         },
         "qmm": qmm,
         "qmv_eager_us_per_call": [round(u, 3) for u in eager_us],
