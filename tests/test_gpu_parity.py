@@ -145,6 +145,16 @@ def test_qmm_block_variants(bits, waves, monkeypatch):
         run_small_linear(M, N, K, bits, group, "bf16", bias, lb.PATH_QMM, seed=bits + N)
 
 
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", range(1, 8))
+def test_qmm_small_m(bits, act):
+    """The MFMA kernel with one or two 16-row tiles (M <= 32) on ragged
+    shapes: rows past M, columns past N, a last K step of 32."""
+    for (M, N, K, group, bias) in [(20, 300, 416, 32, True), (32, 257, 2080, 32, False),
+                                   (3, 130, 160, 32, True), (9, 64, 4096, 128, False)]:
+        run_small_linear(M, N, K, bits, group, act, bias, lb.PATH_QMM, seed=bits + M)
+
+
 @pytest.mark.parametrize("bits", [2, 4, 6])
 def test_qmm_without_workspace(bits):
     """With too little workspace the MFMA path runs without a K split (one
