@@ -80,12 +80,21 @@ struct QmmParams {
   const void* zeros;      // N x groups act
   const void* bias;       // N act or nullptr
   void* y;                // M x N act
-  float* partials;        // split-K: gridDim.z planes of M x N fp32 (workspace)
+  float* partials;        // split-K: gridDim.z planes of fp32 tile records (workspace)
   int M, N, K;
   int groups;             // K / group
   int group_shift;        // log2(group)
   int ksteps_per_split;   // 128-wide K steps per grid.z slice
   int64_t row_bytes;      // K * bits / 8
+};
+// Layout of the split-K partial planes for the reduce kernel: records of
+// 4 fp32 in (tile, wave, row tile, column tile, lane) order, one plane per
+// K split (block tile 16*mtt x 16*nt*waves; mtt, nt, waves powers of two).
+struct QmmReduceShape {
+  int splits;
+  int tiles_n;            // gridDim.x of the main kernel
+  int mtt_shift, nt_shift, wv_shift;
+  int64_t plane_recs;     // records per plane
 };
 // Largest bit width with an 8-wave MFMA kernel instance.
 constexpr int qmm_max_bits_8waves = 5;

@@ -287,7 +287,11 @@ QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   s = std::max<int64_t>(1, std::min<int64_t>(s, std::min<int64_t>(max_split, 64)));
   sc.ksteps_per_split = static_cast<int>((sc.ksteps + s - 1) / s);
   sc.splits = static_cast<int>((sc.ksteps + sc.ksteps_per_split - 1) / sc.ksteps_per_split);
-  if (sc.splits > 1) sc.partial_bytes = static_cast<size_t>(sc.splits) * M * N * sizeof(float);
+  // partial planes cover whole block tiles (the reduce kernel skips the
+  // records past M or N)
+  if (sc.splits > 1)
+    sc.partial_bytes = static_cast<size_t>(sc.splits) * static_cast<size_t>(sc.tiles_n * bn) *
+                       static_cast<size_t>(sc.tiles_m * 16 * sc.mtt) * sizeof(float);
   return sc;
 }
 

@@ -414,57 +414,55 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
   }
 
   // split-K: this block's fp32 partial sums go to plane blockIdx.z of the
-  // workspace; qmm_reduce adds the planes in order.
-  float* part = p.partials + static_cast<int64_t>(blockIdx.z) * p.M * p.N;
+  // workspace in tile order.  A lane's four accumulators of one 16x16 tile
+  // form a 16-byte record; record (tile, wave, mt, nt, lane) sits at
+  // ((((tile * WV + wave) * MTT + mt) * NT + nt) * 64 + lane), so each store
+  // instruction writes 1 KB contiguous per wave and the planes need no
+  // row/column arithmetic.  qmm_reduce_kernel adds the planes in order.
+  const int64_t tile = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  const int64_t plane_recs = static_cast<int64_t>(gridDim.x) * gridDim.y * (WV * MTT * NT * 64);
+  float4_t* part = reinterpret_cast<float4_t*>(p.partials) + blockIdx.z * plane_recs +
+                   (tile * WV + wave) * (MTT * NT * 64) + lane;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = n0 + 16 * NT * wave + 16 * nt + fr;
-    if (n >= p.N) continue;
+  for (int mt = 0; mt < MTT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MTT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * mt + 4 * g + r;
-        if (m < p.M) part[static_cast<int64_t>(m) * p.N + n] = acc[mt][nt][r];
-      }
-  }
+    for (int nt = 0; nt < NT; ++nt) part[(mt * NT + nt) * 64] = acc[mt][nt];
 }
 
-// y = sum over the split planes (in plane order) + bias, rounded once.
-// Each thread produces 4 consecutive outputs of one row.
+// y = sum over the split planes (in plane order) + bias, rounded once.  One
+// thread per 16-byte record of the tile-order planes: D[4g + r][fr] of one
+// 16x16 tile for r = 0..3 (fr = lane & 15, g = lane >> 4).
 template <int ACT>
-__global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, int splits) {
-  const int64_t quads_per_row = (p.N + 3) / 4;
+__global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, QmmReduceShape r) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (q >= quads_per_row * p.M) return;
-  const int m = static_cast<int>(q / quads_per_row);
-  const int n = static_cast<int>(q - static_cast<int64_t>(m) * quads_per_row) * 4;
-  const int64_t plane = static_cast<int64_t>(p.M) * p.N;
-  const int64_t idx = static_cast<int64_t>(m) * p.N + n;
-  const int cnt = min(4, p.N - n);
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  if (cnt == 4 && (p.N % 4) == 0) {
-    // planes are read four at a time so that their loads are in flight together
-    int z = 0;
-    for (; z + 4 <= splits; z += 4) {
-      float4 t[4];
+  if (q >= r.plane_recs) return;
+  const int lane = static_cast<int>(q & 63);
+  const int64_t rec = q >> 6;
+  const int nt = static_cast<int>(rec & ((1 << r.nt_shift) - 1));
+  const int mt = static_cast<int>((rec >> r.nt_shift) & ((1 << r.mtt_shift) - 1));
+  const int w = static_cast<int>((rec >> (r.nt_shift + r.mtt_shift)) & ((1 << r.wv_shift) - 1));
+  const int64_t tile = rec >> (r.nt_shift + r.mtt_shift + r.wv_shift);
+  const int bx = static_cast<int>(tile % r.tiles_n);
+  const int by = static_cast<int>(tile / r.tiles_n);
+  const int n = (bx << (4 + r.nt_shift + r.wv_shift)) + (w << (4 + r.nt_shift)) + (nt << 4) + (lane & 15);
+  const int m = (by << (4 + r.mtt_shift)) + (mt << 4) + 4 * (lane >> 4);
+  if (n >= p.N || m >= p.M) return;
+  const float4_t* src = reinterpret_cast<const float4_t*>(p.partials) + q;
+  // planes are read four at a time so that their loads are in flight together
+  float4_t v = {0.f, 0.f, 0.f, 0.f};
+  int z = 0;
+  for (; z + 4 <= r.splits; z += 4) {
+    float4_t t[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const float4*>(p.partials + (z + u) * plane + idx);
+    for (int u = 0; u < 4; ++u) t[u] = src[(z + u) * r.plane_recs];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { v[0] += t[u].x; v[1] += t[u].y; v[2] += t[u].z; v[3] += t[u].w; }
-    }
-    for (; z < splits; ++z) {
-      const float4 t = *reinterpret_cast<const float4*>(p.partials + z * plane + idx);
-      v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
-    }
-  } else {
-    for (int z = 0; z < splits; ++z)
-      for (int i = 0; i < cnt; ++i) v[i] += p.partials[z * plane + idx + i];
+    for (int u = 0; u < 4; ++u) v += t[u];
   }
-  for (int i = 0; i < cnt; ++i) {
-    const float b = p.bias ? load_act<ACT>(p.bias, n + i) : 0.0f;
-    store_act<ACT>(p.y, idx + i, v[i] + b);
-  }
+  for (; z < r.splits; ++z) v += src[z * r.plane_recs];
+  const float b = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (m + i < p.M) store_act<ACT>(p.y, static_cast<int64_t>(m + i) * p.N + n, v[i] + b);
 }
 
 // Instances: 4-wave blocks for every bit width; 8-wave blocks (256 registers
@@ -509,10 +507,17 @@ hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLa
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || l.grid.z == 1) return e;
-  const int64_t quads = static_cast<int64_t>(p.M) * ((p.N + 3) / 4);
-  const dim3 rgrid(static_cast<unsigned>((quads + 255) / 256));
-  if (act == ACT_F16) qmm_reduce_kernel<ACT_F16><<<rgrid, dim3(256), 0, s>>>(p, l.grid.z);
-  else qmm_reduce_kernel<ACT_BF16><<<rgrid, dim3(256), 0, s>>>(p, l.grid.z);
+  auto log2i = [](int v) { int k = 0; while ((1 << k) < v) ++k; return k; };
+  QmmReduceShape r{};
+  r.splits = static_cast<int>(l.grid.z);
+  r.tiles_n = static_cast<int>(l.grid.x);
+  r.mtt_shift = log2i(l.mtt);
+  r.nt_shift = log2i(l.nt);
+  r.wv_shift = log2i(l.waves);
+  r.plane_recs = static_cast<int64_t>(l.grid.x) * l.grid.y * l.waves * l.mtt * l.nt * 64;
+  const dim3 rgrid(static_cast<unsigned>((r.plane_recs + 255) / 256));
+  if (act == ACT_F16) qmm_reduce_kernel<ACT_F16><<<rgrid, dim3(256), 0, s>>>(p, r);
+  else qmm_reduce_kernel<ACT_BF16><<<rgrid, dim3(256), 0, s>>>(p, r);
   return hipGetLastError();
 }
 
