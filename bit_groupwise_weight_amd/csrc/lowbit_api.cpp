@@ -14,6 +14,7 @@
 #include <atomic>
 #include <mutex>
 #include <string>
+#include <utility>
 
 #include "kernels.h"
 
@@ -78,17 +79,21 @@ lowbit_status check_linear(const void* x, lowbit_dtype act_dtype, const uint8_t*
 }
 
 // One status word pair per device for lowbit_quantize_pack, allocated on first
-// use and kept for the life of the process.
+// use and kept for the life of the process.  A call holds its device's mutex
+// from clearing the word until it has read it back, so concurrent calls on
+// one device (from any threads, on any streams) never see each other's flags.
 constexpr int kMaxDevices = 64;
-std::mutex g_status_mu;
+std::mutex g_status_mu[kMaxDevices];
 int* g_status[kMaxDevices] = {};
 
-lowbit_status device_status_word(int** out) {
+// Current device and its status word; on success *lock holds that device's
+// mutex.
+lowbit_status device_status_word(int** out, std::unique_lock<std::mutex>* lock) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(LOWBIT_ERR_HIP, "device id %d out of range", dev);
-  std::lock_guard<std::mutex> lock(g_status_mu);
+  std::unique_lock<std::mutex> held(g_status_mu[dev]);
   if (g_status[dev] == nullptr) {
     void* p = nullptr;
     e = hipMalloc(&p, 2 * sizeof(int));
@@ -96,6 +101,7 @@ lowbit_status device_status_word(int** out) {
     g_status[dev] = static_cast<int*>(p);
   }
   *out = g_status[dev];
+  *lock = std::move(held);
   return LOWBIT_OK;
 }
 
@@ -377,7 +383,8 @@ lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* status = nullptr;
-  st = device_status_word(&status);
+  std::unique_lock<std::mutex> status_lock;
+  st = device_status_word(&status, &status_lock);
   if (st != LOWBIT_OK) return st;
   hipError_t he = hipMemsetAsync(status, 0, 2 * sizeof(int), s);
   if (he != hipSuccess) return hip_fail(he, "hipMemsetAsync(status)");

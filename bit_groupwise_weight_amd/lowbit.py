@@ -116,11 +116,66 @@ def _stream_handle(device: torch.device, stream) -> Optional[int]:
 
 
 def _require_cuda(*tensors: Optional[torch.Tensor]) -> None:
+    devices = set()
     for t in tensors:
         if t is not None and t.device.type != "cuda":
             raise ValueError("lowbit tensors must live in GPU memory (device 'cuda')")
         if t is not None and not t.is_contiguous():
             raise ValueError("lowbit tensors must be contiguous")
+        if t is not None:
+            devices.add(t.device)
+    if len(devices) > 1:
+        raise ValueError(f"lowbit tensors must all be on one device, got {sorted(map(str, devices))}")
+
+
+def _expect(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+_GROUPS = (32, 64, 128, 256)
+
+
+# The C interface takes raw pointers and cannot see buffer sizes or dtypes;
+# these checks keep every kernel access inside the tensors passed here.
+# (Messages are formatted only on failure: the checks run on every call.)
+def _check_weight_tensors(packed, scales, zeros, N: int, K: int, bits: int, group: int,
+                          sz_dtype: torch.dtype) -> None:
+    if not 1 <= bits <= 7:
+        raise ValueError(f"bits must be in 1..7, got {bits}")
+    if group not in _GROUPS:
+        raise ValueError(f"group must be 32, 64, 128 or 256, got {group}")
+    if K % group:
+        raise ValueError(f"K={K} is not a multiple of group={group}")
+    if packed.dtype != torch.uint8:
+        raise ValueError("packed must be uint8")
+    if packed.numel() != N * K * bits // 8:
+        raise ValueError(f"packed holds {packed.numel()} bytes, expected N*K*bits/8 = {N * K * bits // 8}")
+    G = K // group
+    for name, t in (("scales", scales), ("zeros", zeros)):
+        shp = t.shape
+        if len(shp) != 2 or shp[0] != N or shp[1] != G:
+            raise ValueError(f"{name} must be [{N}, {G}], got {tuple(shp)}")
+        if t.dtype != sz_dtype:
+            raise ValueError(f"{name} must be {sz_dtype}, got {t.dtype}")
+
+
+def _check_linear_tensors(x, packed, scales, zeros, bias, y, bits: int, group: int) -> Tuple[int, int, int]:
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    dt = x.dtype
+    if dt not in _DTYPE_ENUM:
+        raise ValueError(f"x dtype {dt} is not float32, float16 or bfloat16")
+    if scales.dim() != 2:
+        raise ValueError("scales must be 2-D [N, K/group]")
+    M, K = x.shape
+    N = scales.shape[0]
+    _check_weight_tensors(packed, scales, zeros, N, K, bits, group, dt)
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or bias.dtype != dt):
+        raise ValueError(f"bias must be [{N}] of {dt}")
+    if y is not None and (y.dim() != 2 or y.shape[0] != M or y.shape[1] != N or y.dtype != dt):
+        raise ValueError(f"y must be [{M}, {N}] of {dt}")
+    return M, N, K
 
 
 # ---------------------------------------------------------------- C calls --
@@ -159,8 +214,9 @@ def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch
     `out` may give preallocated (packed, scales, zeros, codes) tensors.
     """
     lib = load()
-    if w.dim() != 2:
-        raise ValueError("w must be 2-D [N, K]")
+    _expect(w.dim() == 2, "w must be 2-D [N, K]")
+    _expect(w.dtype == torch.float32, f"w must be float32, got {w.dtype}")
+    _expect(sz_dtype in _DTYPE_ENUM, f"sz_dtype {sz_dtype} is not float32, float16 or bfloat16")
     N, K = w.shape
     if out is None:
         nbytes = lib.lowbit_packed_bytes(bits, N, K)
@@ -173,10 +229,15 @@ def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch
         codes = torch.empty((N, K), dtype=torch.uint8, device=dev) if want_codes else None
     else:
         packed, scales, zeros, codes = out
+    if bits in range(1, 8) and group in (32, 64, 128, 256) and K % group == 0:
+        _check_weight_tensors(packed, scales, zeros, N, K, bits, group, sz_dtype)
+    if codes is not None:
+        _expect(tuple(codes.shape) == (N, K) and codes.dtype == torch.uint8, f"codes must be [{N}, {K}] uint8")
     _require_cuda(w, packed, scales, zeros, codes)
-    st = lib.lowbit_quantize_pack(_ptr(w), bits, group, N, K, _DTYPE_ENUM[sz_dtype], _ptr(scales),
-                                  _ptr(zeros), _ptr(packed), _ptr(codes),
-                                  _stream_handle(w.device, stream))
+    with torch.cuda.device(w.device):
+        st = lib.lowbit_quantize_pack(_ptr(w), bits, group, N, K, _DTYPE_ENUM[sz_dtype], _ptr(scales),
+                                      _ptr(zeros), _ptr(packed), _ptr(codes),
+                                      _stream_handle(w.device, stream))
     _check(st, "lowbit_quantize_pack")
     return packed, scales, zeros, codes
 
@@ -209,10 +270,9 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
     concurrently).
     """
     lib = load()
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D [M, K]")
-    M, K = x.shape
-    N = scales.shape[0]
+    M, N, K = _check_linear_tensors(x, packed, scales, zeros, bias, y, bits, group)
+    if workspace is not None:
+        _expect(workspace.dtype == torch.uint8, "workspace must be uint8")
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     s = _stream_handle(x.device, stream)
@@ -223,12 +283,12 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _DTYPE_ENUM[x.dtype], _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(bias),
             _ptr(y), bits, group, M, N, K, _ptr(workspace), ws_bytes)
-    if path is None:
-        st = lib.lowbit_linear(*args, s)
-        _check(st, "lowbit_linear")
-    else:
-        st = lib.lowbit_linear_path(*args, int(path), s)
-        _check(st, "lowbit_linear_path")
+    with torch.cuda.device(x.device):
+        if path is None:
+            st = lib.lowbit_linear(*args, s)
+        else:
+            st = lib.lowbit_linear_path(*args, int(path), s)
+    _check(st, "lowbit_linear" if path is None else "lowbit_linear_path")
     return y
 
 
@@ -245,16 +305,19 @@ def lowbit_linear_multi(items, bits: int, group: int, stream=None):
     M, dtype = x0.shape[0], x0.dtype
     descs = (LinearDesc * len(items))()
     outs = []
-    for i, (x, packed, scales, zeros, bias, y) in enumerate(items):
-        if x.dim() != 2 or x.shape[0] != M or x.dtype != dtype:
-            raise ValueError("every x must be 2-D with the same M and dtype")
-        N, K = scales.shape[0], x.shape[1]
+    shapes = []
+    for x, packed, scales, zeros, bias, y in items:      # every item is checked before any runs
+        _expect(x.dim() == 2 and x.shape[0] == M and x.dtype == dtype,
+                "every x must be 2-D with the same M and dtype")
+        shapes.append(_check_linear_tensors(x, packed, scales, zeros, bias, y, bits, group))
+    for i, ((x, packed, scales, zeros, bias, y), (_, N, K)) in enumerate(zip(items, shapes)):
         if y is None:
             y = torch.empty((M, N), dtype=dtype, device=x.device)
-        _require_cuda(x, packed, scales, zeros, bias, y)
+        _require_cuda(x0, x, packed, scales, zeros, bias, y)
         descs[i] = LinearDesc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(bias), _ptr(y), N, K)
         outs.append(y)
-    st = lib.lowbit_linear_multi(descs, len(items), _DTYPE_ENUM[dtype], bits, group, M,
-                                 _stream_handle(x0.device, stream))
+    with torch.cuda.device(x0.device):
+        st = lib.lowbit_linear_multi(descs, len(items), _DTYPE_ENUM[dtype], bits, group, M,
+                                     _stream_handle(x0.device, stream))
     _check(st, "lowbit_linear_multi")
     return outs

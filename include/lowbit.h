@@ -108,7 +108,10 @@ int64_t lowbit_num_groups(int64_t K, int group);
  * The call enqueues the work on `stream` and then waits for that stream,
  * because it reports data-dependent errors: LOWBIT_ERR_NONFINITE if w holds a
  * NaN or infinity, LOWBIT_ERR_RANGE if a scale or zero is not finite in
- * sz_dtype.  On either error the output buffers hold unspecified values. */
+ * sz_dtype.  On either error the output buffers hold unspecified values.
+ * Calls from several threads are safe; on one device they run one at a time
+ * (they share the device's status word).  Not for use under stream capture
+ * (it waits for the stream). */
 lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t N, int64_t K,
                                    lowbit_dtype sz_dtype, void* scales, void* zeros,
                                    uint8_t* packed, uint8_t* codes, void* stream);

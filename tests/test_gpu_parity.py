@@ -98,6 +98,40 @@ def test_quantize_errors():
     gpu_quantize(torch.zeros(4, 64), 4, 32, "f16")
 
 
+def test_quantize_concurrent_status():
+    """Calls from two threads on one device, one with a NaN weight and one
+    clean, each report their own status (the per-device status word is held
+    for the whole call), over many rounds on separate streams."""
+    import threading
+    bad = torch.zeros(64, 256)
+    bad[7, 100] = float("nan")
+    good = torch.randn(64, 256) * 0.02
+    errors = []
+
+    def worker(W, want):
+        stream = torch.cuda.Stream(device=DEV)
+        try:
+            with torch.cuda.stream(stream):
+                for _ in range(25):
+                    try:
+                        gpu_quantize(W, 4, 32, "f16", want_codes=False)
+                        got = "LOWBIT_OK"
+                    except lb.LowbitError as e:
+                        got = e.status_name
+                    if got != want:
+                        errors.append((want, got))
+        except Exception as e:   # reported below, not swallowed
+            errors.append(("exception", repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(bad, "LOWBIT_ERR_NONFINITE")),
+               threading.Thread(target=worker, args=(good, "LOWBIT_OK"))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
+
+
 # ---------------------------------------------------------------- linear --
 
 def run_small_linear(M, N, K, bits, group, act, bias, path, seed):
