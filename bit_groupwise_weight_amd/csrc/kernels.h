@@ -53,6 +53,8 @@ struct QmvBatch {
 struct QmvLaunch {
   dim3 grid, block;
   int mt;                 // activation rows per pass: 1, 2 or 4
+  bool pin;               // mt == 1: the register-lean variant (one staged
+                          // fragment live at a time), for many blocks per CU
 };
 // One entry point per bit width (compiled as separate objects).
 hipError_t launch_qmv_b1(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);

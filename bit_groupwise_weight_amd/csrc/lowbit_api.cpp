@@ -231,6 +231,13 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   if (bx > 0x7fffffff || by > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "problem too large");
   l.grid = dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by), static_cast<unsigned>(count));
   l.block = dim3(threads);
+  // With more than four blocks per CU the register-lean variant (one more
+  // wave per SIMD) is 7-9 % faster (b = 4, K x N from 4096 x 14336 to
+  // 16384 x 16384); with fewer the two are within 0.1 us, the other one
+  // slightly ahead (K = N = 4096, bits 1..7).
+  l.pin = total_blocks(threads) * by > 4 * static_cast<int64_t>(device_cus());
+  const int pin_env = env_int("LOWBIT_QMV_PIN", -1);   // (tuning and tests: 0 or 1 forces it)
+  if (pin_env == 0 || pin_env == 1) l.pin = pin_env == 1;
   hipError_t e = kQmv[bits](b, l, group, act_kind(act), stream);
   if (e != hipSuccess) return hip_fail(e, "qmv launch");
   return LOWBIT_OK;
