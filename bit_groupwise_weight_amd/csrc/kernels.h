@@ -35,12 +35,19 @@ struct QmvParams {
   int groups;             // K / group
   int64_t row_bytes;      // K * bits / 8
 };
+// Variants of the decode kernel for one activation row per pass (chosen at
+// launch from the blocks per CU): the default; LEAN, which keeps one staged
+// fragment live at a time (fewer registers, one more wave per SIMD); and
+// LEAN2, LEAN with two rows per lane group at every bit width (more weight
+// bytes in flight per wave).
+enum QmvVariant { QMV_DEFAULT = 0, QMV_LEAN = 1, QMV_LEAN2 = 2 };
 // Rows per row group of the decode kernel for one activation row per pass:
 // two rows for 1, 2, 3 and 5-bit codes, one for 4, 6 and 7 bits (measured on
 // MI355X at K = N = 4096: each choice is 0.1-0.5 us faster than the other
-// there); one row whenever several activation rows share a pass.
-constexpr int qmv_rows_per_group(int bits, int mt) {
-  return (mt == 1 && (bits <= 3 || bits == 5)) ? 2 : 1;
+// there), two for every width in LEAN2; one row whenever several activation
+// rows share a pass.
+constexpr int qmv_rows_per_group(int bits, int mt, int variant) {
+  return mt == 1 && (variant == QMV_LEAN2 || bits <= 3 || bits == 5) ? 2 : 1;
 }
 // Up to kQmvMaxProblems decode problems of one bit width, group size and
 // activation dtype served by one launch: blocks with blockIdx.z == i work on
@@ -53,8 +60,7 @@ struct QmvBatch {
 struct QmvLaunch {
   dim3 grid, block;
   int mt;                 // activation rows per pass: 1, 2 or 4
-  bool pin;               // mt == 1: the register-lean variant (one staged
-                          // fragment live at a time), for many blocks per CU
+  int variant;            // mt == 1: a QmvVariant
 };
 // One entry point per bit width (compiled as separate objects).
 hipError_t launch_qmv_b1(const QmvBatch&, const QmvLaunch&, int group, int act, hipStream_t);

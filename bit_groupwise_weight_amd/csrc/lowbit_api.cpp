@@ -206,38 +206,43 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   if (M >= 2 && 2 * max_per_row <= kQmvStageBudget) l.mt = 2;
   if (M >= 3 && 4 * max_per_row <= kQmvStageBudget) l.mt = 4;
   if (max_per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
-  const int R = lowbit::qmv_rows_per_group(bits, l.mt);
-
   // Block size: 256 threads unless that leaves fewer blocks than CUs.
   int threads = env_int("LOWBIT_QMV_BLOCK", 0);
-  auto blocks_for = [&](int t, int i) {
-    const int64_t rows_per_block = static_cast<int64_t>(t >> b.prob[i].lpr_shift) * R;
+  auto blocks_for = [&](int t, int i, int variant) {
+    const int64_t rows_per_block =
+        static_cast<int64_t>(t >> b.prob[i].lpr_shift) * lowbit::qmv_rows_per_group(bits, l.mt, variant);
     return (probs[i].N + rows_per_block - 1) / rows_per_block;
   };
-  auto total_blocks = [&](int t) {
+  auto total_blocks = [&](int t, int variant) {
     int64_t n = 0;
-    for (int i = 0; i < count; ++i) n += blocks_for(t, i);
+    for (int i = 0; i < count; ++i) n += blocks_for(t, i, variant);
     return n;
   };
   if (threads != 64 && threads != 128 && threads != 256) {
     threads = 256;
-    while (threads > 64 && total_blocks(threads) < device_cus() && (threads >> 1) >= (1 << max_shift))
+    while (threads > 64 && total_blocks(threads, lowbit::QMV_DEFAULT) < device_cus() &&
+           (threads >> 1) >= (1 << max_shift))
       threads >>= 1;
   }
   if (threads < (1 << max_shift)) threads = 1 << max_shift;
-  int64_t bx = 0;
-  for (int i = 0; i < count; ++i) bx = std::max<int64_t>(bx, blocks_for(threads, i));
   const int64_t by = (M + l.mt - 1) / l.mt;
+  // One activation row: with more than four blocks per CU the lean variant
+  // (one more wave per SIMD) gains 7-9 % at b = 4 from 4096 x 14336 to
+  // 16384 x 16384, and where two rows per lane group still leave six or more
+  // blocks per CU, LEAN2 gains another ~10 % (4096 x 28672, 16384 x 16384;
+  // at 3.5-4 blocks per CU it loses 0-3 %).  With fewer blocks the variants
+  // are within 0.1 us, the default slightly ahead (K = N = 4096).
+  const int64_t cus = device_cus();
+  l.variant = lowbit::QMV_DEFAULT;
+  if (l.mt == 1 && total_blocks(threads, lowbit::QMV_DEFAULT) * by > 4 * cus)
+    l.variant = total_blocks(threads, lowbit::QMV_LEAN2) * by >= 6 * cus ? lowbit::QMV_LEAN2 : lowbit::QMV_LEAN;
+  const int var_env = env_int("LOWBIT_QMV_VARIANT", -1);   // (tuning and tests: 0, 1 or 2 forces it)
+  if (l.mt == 1 && var_env >= 0 && var_env <= 2) l.variant = var_env;
+  int64_t bx = 0;
+  for (int i = 0; i < count; ++i) bx = std::max<int64_t>(bx, blocks_for(threads, i, l.variant));
   if (bx > 0x7fffffff || by > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "problem too large");
   l.grid = dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by), static_cast<unsigned>(count));
   l.block = dim3(threads);
-  // With more than four blocks per CU the register-lean variant (one more
-  // wave per SIMD) is 7-9 % faster (b = 4, K x N from 4096 x 14336 to
-  // 16384 x 16384); with fewer the two are within 0.1 us, the other one
-  // slightly ahead (K = N = 4096, bits 1..7).
-  l.pin = total_blocks(threads) * by > 4 * static_cast<int64_t>(device_cus());
-  const int pin_env = env_int("LOWBIT_QMV_PIN", -1);   // (tuning and tests: 0 or 1 forces it)
-  if (pin_env == 0 || pin_env == 1) l.pin = pin_env == 1;
   hipError_t e = kQmv[bits](b, l, group, act_kind(act), stream);
   if (e != hipSuccess) return hip_fail(e, "qmv launch");
   return LOWBIT_OK;

@@ -203,9 +203,9 @@ __device__ __forceinline__ void load_raw_run(const void* x, int64_t off,
 // row group reads one contiguous span of the packed row.  Each lane
 // accumulates, per run, P = sum x*q against activations staged in LDS in the
 // form its bit width needs, then y += s*P + z*X (X = sum of the run's x).
-template <int BITS, int GROUP, int ACT, int MT, bool PIN>
+template <int BITS, int GROUP, int ACT, int MT, int VAR>
 __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint4* stage) {
-  constexpr int R = qmv_rows_per_group(BITS, MT);   // rows per row group
+  constexpr int R = qmv_rows_per_group(BITS, MT, VAR);   // rows per row group
   constexpr int RAW = RawWords<ACT>::n;
   constexpr int QD = RunQuads<ACT, BITS>::n;    // staged quads per run
   constexpr int GSHIFT = GROUP == 32 ? 5 : GROUP == 64 ? 6 : GROUP == 128 ? 7 : 8;
@@ -329,9 +329,9 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
         // time (hoisting them all would take MT*4*QD*4 registers): the empty
         // asm consumes this fragment's sums and, as a memory clobber, keeps
         // the next fragment's LDS reads behind them.  With one row this is
-        // the PIN variant: fewer registers, one more wave per SIMD, which
+        // the lean variants: fewer registers, one more wave per SIMD, which
         // pays when there are many blocks per CU to overlap.
-        if constexpr (MT > 1 || PIN) {
+        if constexpr (MT > 1 || VAR != QMV_DEFAULT) {
 #pragma unroll
           for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[r][m]) : : "memory");
         }
@@ -362,24 +362,24 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
 }
 
 // One problem per launch (its parameters at fixed kernel-argument offsets).
-template <int BITS, int GROUP, int ACT, int MT, bool PIN>
+template <int BITS, int GROUP, int ACT, int MT, int VAR>
 __global__ __launch_bounds__(256) void qmv_kernel(QmvParams p) {
   extern __shared__ uint4 stage[];
-  qmv_block<BITS, GROUP, ACT, MT, PIN>(p, static_cast<int>(blockIdx.x), stage);
+  qmv_block<BITS, GROUP, ACT, MT, VAR>(p, static_cast<int>(blockIdx.x), stage);
 }
 
 // Several problems per launch: blockIdx.z selects the problem (no memory
 // access needed to find it); blocks past that problem's rows exit at once.
-template <int BITS, int GROUP, int ACT, int MT, bool PIN>
+template <int BITS, int GROUP, int ACT, int MT, int VAR>
 __global__ __launch_bounds__(256) void qmv_multi_kernel(QmvBatch b) {
   extern __shared__ uint4 stage[];
   const QmvParams& p = b.prob[blockIdx.z];
-  const int rows_per_block = (static_cast<int>(blockDim.x) >> p.lpr_shift) * qmv_rows_per_group(BITS, MT);
+  const int rows_per_block = (static_cast<int>(blockDim.x) >> p.lpr_shift) * qmv_rows_per_group(BITS, MT, VAR);
   if (static_cast<int>(blockIdx.x) * rows_per_block >= p.N) return;   // block-uniform
-  qmv_block<BITS, GROUP, ACT, MT, PIN>(p, static_cast<int>(blockIdx.x), stage);
+  qmv_block<BITS, GROUP, ACT, MT, VAR>(p, static_cast<int>(blockIdx.x), stage);
 }
 
-template <int GROUP, int ACT, int MT, bool PIN>
+template <int GROUP, int ACT, int MT, int VAR>
 static hipError_t launch_one(const QmvBatch& b, const QmvLaunch& l, hipStream_t s) {
   // staged runs (sized for the widest lane group) plus one scratch run for
   // threads without a run
@@ -388,18 +388,23 @@ static hipError_t launch_one(const QmvBatch& b, const QmvLaunch& l, hipStream_t 
   const size_t lds = (static_cast<size_t>(MT) * 4 * (size_t(1) << shift) + 1) *
                      RunQuads<ACT, LOWBIT_BITS>::n * 16;
   if (l.grid.z == 1)
-    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, PIN><<<l.grid, l.block, lds, s>>>(b.prob[0]);
+    qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, VAR><<<l.grid, l.block, lds, s>>>(b.prob[0]);
   else
-    qmv_multi_kernel<LOWBIT_BITS, GROUP, ACT, MT, PIN><<<l.grid, l.block, lds, s>>>(b);
+    qmv_multi_kernel<LOWBIT_BITS, GROUP, ACT, MT, VAR><<<l.grid, l.block, lds, s>>>(b);
   return hipGetLastError();
 }
 
 template <int GROUP, int ACT>
 static hipError_t dispatch_mt(const QmvBatch& p, const QmvLaunch& l, hipStream_t s) {
   switch (l.mt) {
-    case 1: return l.pin ? launch_one<GROUP, ACT, 1, true>(p, l, s) : launch_one<GROUP, ACT, 1, false>(p, l, s);
-    case 2: return launch_one<GROUP, ACT, 2, true>(p, l, s);
-    case 4: return launch_one<GROUP, ACT, 4, true>(p, l, s);
+    case 1:
+      // (LEAN2 is LEAN where the default already has two rows per group)
+      if (l.variant == QMV_LEAN2 && qmv_rows_per_group(LOWBIT_BITS, 1, QMV_DEFAULT) == 1)
+        return launch_one<GROUP, ACT, 1, QMV_LEAN2>(p, l, s);
+      if (l.variant != QMV_DEFAULT) return launch_one<GROUP, ACT, 1, QMV_LEAN>(p, l, s);
+      return launch_one<GROUP, ACT, 1, QMV_DEFAULT>(p, l, s);
+    case 2: return launch_one<GROUP, ACT, 2, QMV_LEAN>(p, l, s);
+    case 4: return launch_one<GROUP, ACT, 4, QMV_LEAN>(p, l, s);
     default: return hipErrorInvalidValue;
   }
 }
