@@ -41,11 +41,11 @@ ROTATE_BYTES = 1 << 30
 # kernel sources whose sha256 prefix is `src_hash`; for any other sources bench
 # reports traffic as null.
 MEASURED_TRAFFIC = {
-    "src_hash": "395143a743eace32",
-    "qmv_bits1to7_bytes": 67358245,
-    "qmm_bytes": {"4096x14336": 102181979, "14336x4096": 95402941},
+    "src_hash": "fd725df71bc0424b",
+    "qmv_bits1to7_bytes": 67363653,
+    "qmm_bytes": {"4096x14336": 102182115, "14336x4096": 95403274},
     # rocprofv3 MfmaUtil (%) of the main MFMA kernel per shape
-    "qmm_mfma_util": {"4096x14336": 18.33, "14336x4096": 16.54},
+    "qmm_mfma_util": {"4096x14336": 18.58, "14336x4096": 16.53},
 }
 
 
