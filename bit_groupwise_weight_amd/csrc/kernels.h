@@ -104,13 +104,18 @@ struct QmmReduceShape {
   int mtt_shift, nt_shift, wv_shift;
   int64_t plane_recs;     // records per plane
 };
-// Largest bit width with an 8-wave MFMA kernel instance.
+// Largest bit widths with an 8-wave MFMA kernel instance: 8 column waves,
+// and 4 column waves in two K groups (whose super-step activations take more
+// registers).
 constexpr int qmm_max_bits_8waves = 5;
+constexpr int qmm_max_bits_kgroups = 4;
 struct QmmLaunch {
   dim3 grid;              // (ceil(N/(16*nt*waves)), ceil(M/(16*mtt)), k-splits)
   int mtt;                // 16-row MFMA tiles per block: 1, 2, 4 or 8
   int nt;                 // 16-column MFMA tiles per wave (2)
-  int waves;              // waves per block: 4, or 8 (bits <= qmm_max_bits_8waves)
+  int waves;              // column waves per block: 4, or 8 (bits <= qmm_max_bits_8waves)
+  int kgroups;            // K groups per block: 1, or 2 with 4 column waves
+                          // (bits <= qmm_max_bits_kgroups); waves*kgroups waves in all
 };
 hipError_t launch_qmm_b1(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b2(const QmmParams&, const QmmLaunch&, int act, hipStream_t);

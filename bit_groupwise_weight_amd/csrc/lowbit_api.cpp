@@ -269,11 +269,47 @@ const QmmLauncher kQmm[8] = {nullptr,
 // Schedule of the MFMA kernel: block tile (16*mtt) x (16*nt*waves), K steps
 // of 128, and a K split that fills the CUs with one block each.
 struct QmmSchedule {
-  int mtt, nt, waves;
+  int mtt, nt, waves, kgroups;
   int64_t tiles_n, tiles_m, ksteps;
   int splits, ksteps_per_split;
-  size_t partial_bytes;
+  size_t partial_bytes;   // fp32 partial planes (split-K)
 };
+
+// Block tiles and K split for column tile width 16*nt*waves: one block per
+// CU (each block takes a whole CU's register file), K split just enough that
+// the tiles times the splits fill the CUs without a second, partial wave of
+// blocks (LOWBIT_QMM_BLOCKS overrides the block target for tuning).
+void qmm_split(QmmSchedule& sc, int64_t M, int64_t N, int64_t K) {
+  const int64_t bn = 16 * sc.nt * sc.waves;
+  sc.tiles_n = (N + bn - 1) / bn;
+  sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
+  sc.ksteps = (K + 127) / 128;
+  const int64_t target = env_int("LOWBIT_QMM_BLOCKS", device_cus());
+  const int64_t tiles = sc.tiles_n * sc.tiles_m;
+  int64_t s = std::max<int64_t>(1, target / tiles);
+  const int64_t max_split = std::max<int64_t>(1, sc.ksteps / 2);   // >= 2 steps per split
+  s = std::max<int64_t>(1, std::min<int64_t>(s, std::min<int64_t>(max_split, 64)));
+  sc.ksteps_per_split = static_cast<int>((sc.ksteps + s - 1) / s);
+  // with two K groups, an even step count per split keeps the groups equal
+  if (sc.kgroups == 2 && sc.ksteps_per_split % 2 == 1 && sc.ksteps_per_split < sc.ksteps)
+    ++sc.ksteps_per_split;
+  sc.splits = static_cast<int>((sc.ksteps + sc.ksteps_per_split - 1) / sc.ksteps_per_split);
+  // partial planes cover whole block tiles (the reduce kernel skips the
+  // records past M or N)
+  sc.partial_bytes = 0;
+  if (sc.splits > 1)
+    sc.partial_bytes = static_cast<size_t>(sc.splits) * static_cast<size_t>(sc.tiles_n * bn) *
+                       static_cast<size_t>(sc.tiles_m * 16 * sc.mtt) * sizeof(float);
+}
+
+// Steps per block at or below which 64-column blocks (one column tile per
+// wave) beat 128-column ones at M = 128: the narrower tile halves the K split
+// (no reduce kernel at all for N = 14336 with K <= 4096) at the price of
+// twice the LDS reads per MFMA, which only pays while the loop is short
+// (measured, N = 14336: K = 1024 13.1 vs 21.2 us, K = 2048 20.1 vs 24.7,
+// K = 4096 even, K = 8192 62.7 vs 55.7; N = 4096: K = 7168 22.7 vs 24.4,
+// K = 14336 36.0 vs 33.3).
+constexpr int kQmmNarrowMaxSteps = 16;
 
 QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
@@ -287,29 +323,26 @@ QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   // per CU than 4-wave blocks at M = 128, K = 4096, N = 14336), but the wider
   // tile needs twice the K splits, whose partial planes cost more than that
   // gain once the split exceeds ~4 (N = 4096 is faster with 4-wave blocks).
+  // Two K groups of 4 column waves (8 waves, 128 columns) keep two waves per
+  // SIMD at the tile width of a 4-wave block, so the K split across blocks
+  // stays that of the 4-wave block; used for full 128-row tiles up to 4 bits.
+  // (LOWBIT_QMM_MTT, LOWBIT_QMM_KGROUPS, LOWBIT_QMM_WAVES and LOWBIT_QMM_NT
+  // override the choices for tuning; LOWBIT_QMM_WAVES applies with one K
+  // group, LOWBIT_QMM_NT with two.)
   const bool can8 = bits <= lowbit::qmm_max_bits_8waves;
+  const bool can_kg = bits <= lowbit::qmm_max_bits_kgroups;
+  const int kg_default = (can_kg && sc.mtt == 8) ? 2 : 1;
+  sc.kgroups = (can_kg && env_int("LOWBIT_QMM_KGROUPS", kg_default) == 2) ? 2 : 1;
   const int wv_default = (can8 && sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
-  // (LOWBIT_QMM_MTT and LOWBIT_QMM_WAVES override the choices for tuning)
-  sc.waves = (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
-  const int64_t bn = 16 * sc.nt * sc.waves;
-  sc.tiles_n = (N + bn - 1) / bn;
-  sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
-  sc.ksteps = (K + 127) / 128;
-  // One block per CU (each block takes a whole CU's register file): split K
-  // just enough that the tiles times the splits fill the CUs without a
-  // second, partial wave of blocks.
-  const int64_t target = env_int("LOWBIT_QMM_BLOCKS", device_cus());
-  const int64_t tiles = sc.tiles_n * sc.tiles_m;
-  int64_t s = std::max<int64_t>(1, target / tiles);
-  const int64_t max_split = std::max<int64_t>(1, sc.ksteps / 2);   // >= 2 steps per split
-  s = std::max<int64_t>(1, std::min<int64_t>(s, std::min<int64_t>(max_split, 64)));
-  sc.ksteps_per_split = static_cast<int>((sc.ksteps + s - 1) / s);
-  sc.splits = static_cast<int>((sc.ksteps + sc.ksteps_per_split - 1) / sc.ksteps_per_split);
-  // partial planes cover whole block tiles (the reduce kernel skips the
-  // records past M or N)
-  if (sc.splits > 1)
-    sc.partial_bytes = static_cast<size_t>(sc.splits) * static_cast<size_t>(sc.tiles_n * bn) *
-                       static_cast<size_t>(sc.tiles_m * 16 * sc.mtt) * sizeof(float);
+  sc.waves = sc.kgroups == 2 ? 4 : (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
+  if (sc.kgroups == 2 && sc.mtt == 8) {
+    QmmSchedule narrow = sc;
+    narrow.nt = 1;
+    qmm_split(narrow, M, N, K);
+    const int nt_env = env_int("LOWBIT_QMM_NT", 0);
+    if (nt_env == 1 || (nt_env != 2 && narrow.ksteps_per_split <= kQmmNarrowMaxSteps)) return narrow;
+  }
+  qmm_split(sc, M, N, K);
   return sc;
 }
 
@@ -340,6 +373,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   l.mtt = sc.mtt;
   l.nt = sc.nt;
   l.waves = sc.waves;
+  l.kgroups = sc.kgroups;
   l.grid = dim3(static_cast<unsigned>(sc.tiles_n), static_cast<unsigned>(sc.tiles_m),
                 static_cast<unsigned>(sc.splits));
   hipError_t e = kQmm[bits](p, l, act_kind(act), stream);

@@ -25,6 +25,13 @@
 //   * codes are loaded two steps ahead; the MFMAs of each k-sub are issued
 //     in a fixed order with the dequantization of the next k-sub spread
 //     between them;
+//   * K split inside the block (KGR = 2): two groups of waves share the
+//     block tile and take alternate K steps; one LDS stage then holds the
+//     tiles of both steps, and at the end the second group's accumulators
+//     are added to the first group's through LDS (fixed order).  Two waves
+//     per SIMD at the column width of a 4-wave block: one wave's
+//     dequantization runs under the other's MFMAs without the wider tile
+//     that would double the K split across blocks;
 //   * split-K: blocks along grid.z own disjoint K ranges; with S > 1 each
 //     block writes an fp32 partial plane to the workspace and a second small
 //     kernel adds the planes in fixed order (results do not depend on
@@ -170,39 +177,49 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
-// One block: 16*MTT rows x 16*NT*WV columns, WV waves (4 or 8); wave w owns
-// columns [16*NT*w, 16*NT*(w+1)) as NT 16-wide MFMA tiles and all rows.  One
-// block per CU: with 4 waves each wave has a whole SIMD's registers; with 8,
-// two waves share a SIMD, so one wave's dequantization can run while the
+// One block: 16*MTT rows x 16*NT*WC columns, WC column waves times KGR K
+// groups (WV = WC*KGR waves, 4 or 8).  Column wave c owns columns
+// [16*NT*c, 16*NT*(c+1)) as NT 16-wide MFMA tiles and all rows; K group kg
+// takes steps s_begin + KGR*u + kg (u = 0, 1, ...: the block's super-steps).
+// One block per CU: with 4 waves each wave has a whole SIMD's registers; with
+// 8, two waves share a SIMD, so one wave's dequantization can run while the
 // other's MFMAs execute.
-template <int BITS, int ACT, int MTT, int NT, int WV>
-__global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
-  constexpr int STAGE = MTT * 16 * 16;   // uint4 per activation stage (16*MTT rows x 256 B)
+template <int BITS, int ACT, int MTT, int NT, int WC, int KGR>
+__global__ __launch_bounds__(64 * WC * KGR, 1) void qmm_kernel(QmmParams p) {
+  constexpr int WV = WC * KGR;
+  constexpr int STAGE = MTT * 16 * 16;   // uint4 per step's activation tile (16*MTT rows x 256 B)
   constexpr int MH = MTT > 1 ? MTT / 2 : 1;   // activation fragments are refilled in two halves
-  __shared__ uint4 stage0[STAGE];
-  __shared__ uint4 stage1[STAGE];
+  // two stages of KGR step tiles each
+  __shared__ uint4 lds[2 * KGR * STAGE];
+  uint4* const stage0 = lds;
+  uint4* const stage1 = lds + KGR * STAGE;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int cw = wave % WC;           // column wave
+  const int kg = wave / WC;           // K group
   const int lane = tid & 63;
   const int fr = lane & 15;           // row / column inside a 16-wide MFMA tile
   const int g = lane >> 4;            // lane group: K positions [32g, 32g+32) of a step
-  const int n0 = blockIdx.x * (16 * NT * WV);
+  const int n0 = blockIdx.x * (16 * NT * WC);
   // activation row quads (4 rows x 256 bytes = one load instruction per wave)
-  // per step, and how many of them each wave loads
+  // per step, and how many of a super-step's KGR*RQ each wave loads
   constexpr int RQ = 4 * MTT;
-  constexpr int XL = (RQ + WV - 1) / WV;
+  constexpr int XL = (KGR * RQ + WV - 1) / WV;
   const int m0 = blockIdx.y * (16 * MTT);
   const int ksteps = (p.K + QMM_BK - 1) / QMM_BK;
   const int s_begin = blockIdx.z * p.ksteps_per_split;
   const int s_end = min(ksteps, s_begin + p.ksteps_per_split);
+  const int supers = (s_end - s_begin + KGR - 1) / KGR;
+  // this wave's K step in super-step u
+  auto wstep = [&](int u) { return s_begin + KGR * u + kg; };
 
   // ---- this lane's weight rows (clamped; columns past N get s = z = 0)
   int64_t wrow[NT], szrow[NT];
   uint32_t nok[NT];   // all ones for a real column, 0 past N
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int n = n0 + 16 * NT * wave + 16 * nt + fr;
+    const int n = n0 + 16 * NT * cw + 16 * nt + fr;
     nok[nt] = 0u - static_cast<uint32_t>(n < p.N);
     const int nc = min(n, p.N - 1);
     wrow[nt] = static_cast<int64_t>(nc) * p.row_bytes;
@@ -242,34 +259,40 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
     }
   };
 
-  // Activation stage: the 16*MTT x 128 tile of one step, rows of 256 bytes
-  // (16 chunks of 8 elements) with chunk c of row r stored at position
-  // c ^ stage_swizzle(r & 15) (see there).  Load i of wave w covers row quad
-  // q = WV*i + w (rows 4q .. 4q+3; quads past the tile are skipped): lane l
-  // fetches the chunk that belongs at position l & 15 of row 4q + l/16, and
-  // later stores it at byte 16 l of those four rows.  Rows past M and chunks past K read a clamped in-range address: such
-  // a row only feeds output rows that are never stored, and past K the
-  // weights are dequantized with s = z = 0.
+  // Activation stage: the 16*MTT x 128 tiles of a super-step's KGR steps
+  // (tile j at uint4 offset j*STAGE), rows of 256 bytes (16 chunks of 8
+  // elements) with chunk c of row r stored at position c ^ stage_swizzle(r & 15)
+  // (see there).  Load i of wave w covers quad q = WV*i + w of the stage: step
+  // j = q / RQ of the super-step, row quad q % RQ (rows 4(q%RQ) .. +3; quads
+  // past the stage are skipped): lane l fetches the chunk that belongs at
+  // position l & 15 of row 4(q%RQ) + l/16, and later stores it at byte 16 l
+  // of quad q.  Rows past M and chunks past K read a clamped in-range
+  // address: such a row only feeds output rows that are never stored, and
+  // past K (or past the block's last step) the weights are dequantized with
+  // s = z = 0.
   const uint16_t* xrow[XL];
-  int xchunk[XL];
+  int xchunk[XL], xstep[XL];
 #pragma unroll
   for (int i = 0; i < XL; ++i) {
-    const int row = min(4 * (WV * i + wave), 16 * MTT - 4) + (lane >> 4);
+    const int q = min(WV * i + wave, KGR * RQ - 1);
+    const int row = 4 * (q % RQ) + (lane >> 4);
+    xstep[i] = q / RQ;
     xchunk[i] = 8 * ((lane & 15) ^ stage_swizzle(row & 15));
     xrow[i] = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.K;
   }
   // (native vectors: HIP's uint4 is a struct whose copies become memcpys
   // that keep these arrays out of registers)
-  auto load_x = [&](int step, u32x4_t (&xr)[XL]) {
-    const int kb = min(step, s_end - 1) * QMM_BK;
+  auto load_x = [&](int u, u32x4_t (&xr)[XL]) {
 #pragma unroll
-    for (int i = 0; i < XL; ++i)
+    for (int i = 0; i < XL; ++i) {
+      const int kb = min(s_begin + KGR * u + xstep[i], s_end - 1) * QMM_BK;
       xr[i] = *reinterpret_cast<const u32x4_t*>(xrow[i] + min(kb + xchunk[i], p.K - 8));
+    }
   };
   auto store_x = [&](const u32x4_t (&xr)[XL], uint4* stage) {
 #pragma unroll
     for (int i = 0; i < XL; ++i)
-      if (RQ % WV == 0 || WV * i + wave < RQ)    // wave-uniform
+      if ((KGR * RQ) % WV == 0 || WV * i + wave < KGR * RQ)    // wave-uniform
         reinterpret_cast<u32x4_t*>(stage)[(WV * i + wave) * 64 + lane] = xr[i];
   };
 
@@ -282,11 +305,13 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
   uint4 af[MTT];           // activation operands of one k-sub: [row tile]
 
   // activation operands of row tiles [MT0, MT1) for k-sub KS
+  // (from this K group's tile of the stage)
   auto read_a = [&](const uint4* stage, auto KSc, auto MT0c, auto MT1c) {
     constexpr int KS = decltype(KSc)::value;
+    const uint4* t = stage + (KGR > 1 ? kg * STAGE : 0);
     static_for<decltype(MT1c)::value - decltype(MT0c)::value>([&](auto ic) {
       constexpr int mt = decltype(MT0c)::value + decltype(ic)::value;
-      af[mt] = stage[(16 * mt + fr) * 16 + ((4 * g + KS) ^ stage_swizzle(fr))];
+      af[mt] = t[(16 * mt + fr) * 16 + ((4 * g + KS) ^ stage_swizzle(fr))];
     });
   };
   using I0 = std::integral_constant<int, 0>;
@@ -335,42 +360,47 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
   using K2 = std::integral_constant<int, 2>;
   using K3 = std::integral_constant<int, 3>;
 
-  // Pipeline over K steps, with two register sets (A, B) for codes and
-  // activations: step t reads LDS stage t%2; in its first phase it loads the
-  // activations of step t+2 and, once k-sub 3 of its own codes is
-  // dequantized, the codes of step t+2; it stores the activations of step
-  // t+1 into the other stage and meets the other waves once that stage is
-  // written and its own is fully read, then reads the first operands of
-  // step t+1 during its last phase.  Weight operands are dequantized one
-  // k-sub ahead, in place: k-sub 3 of step t during phase 0, k-subs 0..2 of
-  // step t+1 during phases 1..3.  All loads are ordinary loads that
-  // complete in order, so every use waits only for the loads it needs.
+  // Pipeline over super-steps (one K step per wave each), with two register
+  // sets (A, B) for codes and activations: super-step u reads LDS stage u%2;
+  // in its first phase it loads the activations of super-step u+2 and, once
+  // k-sub 3 of its own codes is dequantized, this wave's codes of super-step
+  // u+2; it stores the activations of super-step u+1 into the other stage
+  // and meets the other waves once that stage is written and its own is fully
+  // read, then reads the first operands of super-step u+1 during its last
+  // phase.  Weight operands are dequantized one k-sub ahead, in place: k-sub
+  // 3 of step u during phase 0, k-subs 0..2 of step u+1 during phases 1..3.
+  // With two K groups a super-step's activations take twice the registers,
+  // so they use one register set: loaded one super-step ahead and stored
+  // just before the barrier.  All loads are ordinary loads that complete in
+  // order, so every use waits only for the loads it needs.
+  constexpr bool X1 = KGR > 1;
 #define LOWBIT_QMM_STEP(S_, SR, SW, XLD, XST, CUR, NXT)                                       \
   {                                                                                           \
-    load_x((S_) + 2, XLD);                                                                    \
+    load_x((S_) + (X1 ? 1 : 2), XLD);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     {                                                                                         \
       float sv[NT], zv[NT];                                                                   \
       scale_zero(CUR, sv, zv);                                                                \
       phase(K0{}, K3{}, CUR, sv, zv, SR, K1{});                                               \
     }                                                                                         \
-    load_codes((S_) + 2, CUR);                                                                \
+    load_codes(wstep((S_) + 2), CUR);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     float sv[NT], zv[NT];                                                                     \
     scale_zero(NXT, sv, zv);                                                                  \
     phase(K1{}, K0{}, NXT, sv, zv, SR, K2{});                                                 \
-    store_x(XST, SW);                                                                         \
+    if constexpr (!X1) store_x(XST, SW);                                                      \
     phase(K2{}, K1{}, NXT, sv, zv, SR, K3{});                                                 \
+    if constexpr (X1) store_x(XLD, SW);                                                       \
     __syncthreads(); /* stage S_+1 written by every wave; stage S_ fully read */              \
     phase(K3{}, K2{}, NXT, sv, zv, SW, K0{});                                                 \
   }
 
   Codes ca, cb;
   u32x4_t xa[XL], xb[XL];
-  load_x(s_begin, xa);
-  load_x(s_begin + 1, xb);
-  load_codes(s_begin, ca);
-  load_codes(s_begin + 1, cb);
+  load_x(0, xa);
+  if constexpr (!X1) load_x(1, xb);
+  load_codes(wstep(0), ca);
+  load_codes(wstep(1), cb);
   store_x(xa, stage0);
   {
     float sv[NT], zv[NT];
@@ -387,19 +417,55 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
   }
   __syncthreads();
   read_a(stage0, K0{}, I0{}, IMTT{});
-  int s = s_begin;
-  for (; s + 2 <= s_end; s += 2) {
-    LOWBIT_QMM_STEP(s, stage0, stage1, xa, xb, ca, cb)
-    LOWBIT_QMM_STEP(s + 1, stage1, stage0, xb, xa, cb, ca)
+  int u = 0;
+  if constexpr (X1) {
+    for (; u + 2 <= supers; u += 2) {
+      LOWBIT_QMM_STEP(u, stage0, stage1, xa, xa, ca, cb)
+      LOWBIT_QMM_STEP(u + 1, stage1, stage0, xa, xa, cb, ca)
+    }
+    if (u < supers) LOWBIT_QMM_STEP(u, stage0, stage1, xa, xa, ca, cb)
+  } else {
+    for (; u + 2 <= supers; u += 2) {
+      LOWBIT_QMM_STEP(u, stage0, stage1, xa, xb, ca, cb)
+      LOWBIT_QMM_STEP(u + 1, stage1, stage0, xb, xa, cb, ca)
+    }
+    if (u < supers) LOWBIT_QMM_STEP(u, stage0, stage1, xa, xb, ca, cb)
   }
-  if (s < s_end) LOWBIT_QMM_STEP(s, stage0, stage1, xa, xb, ca, cb)
 #undef LOWBIT_QMM_STEP
 
-  // ---- epilogue.  Lane holds D[4*g + r][fr] of each 16x16 tile.
-  if (gridDim.z == 1) {
+  if constexpr (KGR > 1) {
+    // K groups 1.. hand their sums to group 0 through LDS (the stages are no
+    // longer read once every wave is past this barrier); group 0 adds them in
+    // group order.  A lane's record (cw, mt, nt) sits at
+    // ((cw * MTT + mt) * NT + nt) * 64 + lane of its group's region.
+    static_assert((KGR - 1) * WC * MTT * NT * 64 <= 2 * KGR * STAGE, "K-group sums exceed LDS");
+    float4_t* red = reinterpret_cast<float4_t*>(lds);
+    __syncthreads();
+    if (kg > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          red[((((kg - 1) * WC + cw) * MTT + mt) * NT + nt) * 64 + lane] = acc[mt][nt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 1; j < KGR; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] += red[((((j - 1) * WC + cw) * MTT + mt) * NT + nt) * 64 + lane];
+  }
+
+  // ---- epilogue.  Lane holds D[4*g + r][fr] of each 16x16 tile; with K
+  // groups only group 0 holds the block's sums (the other groups stay for
+  // the barriers below and store nothing).
+  const bool holder = (KGR == 1) || kg == 0;
+  auto store_y = [&](const float4_t (&v)[MTT][NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int n = n0 + 16 * NT * wave + 16 * nt + fr;
+      const int n = n0 + 16 * NT * cw + 16 * nt + fr;
       if (n >= p.N) continue;
       const float bias = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
 #pragma unroll
@@ -407,26 +473,31 @@ __global__ __launch_bounds__(64 * WV, 1) void qmm_kernel(QmmParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + 16 * mt + 4 * g + r;
-          if (m < p.M) store_act<ACT>(p.y, static_cast<int64_t>(m) * p.N + n, acc[mt][nt][r] + bias);
+          if (m < p.M) store_act<ACT>(p.y, static_cast<int64_t>(m) * p.N + n, v[mt][nt][r] + bias);
         }
     }
+  };
+  if (gridDim.z == 1) {
+    if (holder) store_y(acc);
     return;
   }
 
   // split-K: this block's fp32 partial sums go to plane blockIdx.z of the
   // workspace in tile order.  A lane's four accumulators of one 16x16 tile
   // form a 16-byte record; record (tile, wave, mt, nt, lane) sits at
-  // ((((tile * WV + wave) * MTT + mt) * NT + nt) * 64 + lane), so each store
+  // ((((tile * WC + wave) * MTT + mt) * NT + nt) * 64 + lane), so each store
   // instruction writes 1 KB contiguous per wave and the planes need no
-  // row/column arithmetic.  qmm_reduce_kernel adds the planes in order.
+  // row/column arithmetic (wave = the column wave).  qmm_reduce_kernel adds
+  // the planes in order.
   const int64_t tile = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
-  const int64_t plane_recs = static_cast<int64_t>(gridDim.x) * gridDim.y * (WV * MTT * NT * 64);
-  float4_t* part = reinterpret_cast<float4_t*>(p.partials) + blockIdx.z * plane_recs +
-                   (tile * WV + wave) * (MTT * NT * 64) + lane;
+  const int64_t plane_recs = static_cast<int64_t>(gridDim.x) * gridDim.y * (WC * MTT * NT * 64);
+  float4_t* part = reinterpret_cast<float4_t*>(p.partials) + (tile * WC + cw) * (MTT * NT * 64) + lane;
+  if (holder) {
 #pragma unroll
-  for (int mt = 0; mt < MTT; ++mt)
+    for (int mt = 0; mt < MTT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) part[(mt * NT + nt) * 64] = acc[mt][nt];
+      for (int nt = 0; nt < NT; ++nt) part[blockIdx.z * plane_recs + (mt * NT + nt) * 64] = acc[mt][nt];
+  }
 }
 
 // y = sum over the split planes (in plane order) + bias, rounded once.  One
@@ -465,17 +536,33 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, QmmReduceS
     if (m + i < p.M) store_act<ACT>(p.y, static_cast<int64_t>(m + i) * p.N + n, v[i] + b);
 }
 
-// Instances: 4-wave blocks for every bit width; 8-wave blocks (256 registers
-// per wave) for bit widths up to qmm_max_bits_8waves, above which the code
+// Instances: 4 column waves (one K group) for every bit width; 8 waves (256
+// registers per wave) -- 8 column waves up to qmm_max_bits_8waves, 4 column
+// waves in two K groups up to qmm_max_bits_kgroups -- above which the code
 // registers of the pipeline no longer fit without spilling.
 template <int ACT, int MTT>
-static hipError_t launch_mtt(const QmmParams& p, int nt, int waves, dim3 grid, hipStream_t s) {
-  if (nt != 2) return hipErrorInvalidValue;
-  if (waves == 4) {
-    qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 4><<<grid, dim3(256), 0, s>>>(p);
-  } else if (waves == 8) {
+static hipError_t launch_mtt(const QmmParams& p, const QmmLaunch& l, hipStream_t s) {
+  if (l.nt == 1) {
+    if constexpr (LOWBIT_BITS <= qmm_max_bits_kgroups && MTT == 8) {
+      if (l.waves == 4 && l.kgroups == 2) {
+        qmm_kernel<LOWBIT_BITS, ACT, MTT, 1, 4, 2><<<l.grid, dim3(512), 0, s>>>(p);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  if (l.nt != 2) return hipErrorInvalidValue;
+  if (l.waves == 4 && l.kgroups == 1) {
+    qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 4, 1><<<l.grid, dim3(256), 0, s>>>(p);
+  } else if (l.waves == 8 && l.kgroups == 1) {
     if constexpr (LOWBIT_BITS <= qmm_max_bits_8waves) {
-      qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 8><<<grid, dim3(512), 0, s>>>(p);
+      qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 8, 1><<<l.grid, dim3(512), 0, s>>>(p);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (l.waves == 4 && l.kgroups == 2) {
+    if constexpr (LOWBIT_BITS <= qmm_max_bits_kgroups) {
+      qmm_kernel<LOWBIT_BITS, ACT, MTT, 2, 4, 2><<<l.grid, dim3(512), 0, s>>>(p);
     } else {
       return hipErrorInvalidValue;
     }
@@ -486,12 +573,12 @@ static hipError_t launch_mtt(const QmmParams& p, int nt, int waves, dim3 grid, h
 }
 
 template <int ACT>
-static hipError_t launch_act(const QmmParams& p, int mtt, int nt, int waves, dim3 grid, hipStream_t s) {
-  switch (mtt) {
-    case 1: return launch_mtt<ACT, 1>(p, nt, waves, grid, s);
-    case 2: return launch_mtt<ACT, 2>(p, nt, waves, grid, s);
-    case 4: return launch_mtt<ACT, 4>(p, nt, waves, grid, s);
-    case 8: return launch_mtt<ACT, 8>(p, nt, waves, grid, s);
+static hipError_t launch_act(const QmmParams& p, const QmmLaunch& l, hipStream_t s) {
+  switch (l.mtt) {
+    case 1: return launch_mtt<ACT, 1>(p, l, s);
+    case 2: return launch_mtt<ACT, 2>(p, l, s);
+    case 4: return launch_mtt<ACT, 4>(p, l, s);
+    case 8: return launch_mtt<ACT, 8>(p, l, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -502,8 +589,8 @@ hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLa
                                                  hipStream_t s) {
   hipError_t e;
   switch (act) {
-    case ACT_F16: e = launch_act<ACT_F16>(p, l.mtt, l.nt, l.waves, l.grid, s); break;
-    case ACT_BF16: e = launch_act<ACT_BF16>(p, l.mtt, l.nt, l.waves, l.grid, s); break;
+    case ACT_F16: e = launch_act<ACT_F16>(p, l, s); break;
+    case ACT_BF16: e = launch_act<ACT_BF16>(p, l, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || l.grid.z == 1) return e;

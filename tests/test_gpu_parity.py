@@ -194,16 +194,92 @@ def test_qmv_register_variants(bits, act, monkeypatch):
             assert torch.equal(outs[0], y), f"variants differ: N={N} K={K} b={bits} {act}"
 
 
-@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("waves,kgroups,nt", [("4", "1", "2"), ("8", "1", "2"), ("4", "2", "2"),
+                                               ("4", "2", "1")])
 @pytest.mark.parametrize("bits", [1, 3, 4, 5, 7])
-def test_qmm_block_variants(bits, waves, monkeypatch):
-    """Both MFMA block shapes (4 waves x 128 columns, 8 waves x 256 columns;
-    8-wave instances exist up to 5 bits, above that the 4-wave kernel runs)
-    on ragged shapes: rows past M, columns past N, a last K step of 32."""
+def test_qmm_block_variants(bits, waves, kgroups, nt, monkeypatch):
+    """Every MFMA block shape (4 waves x 128 columns; 8 waves x 256 columns;
+    4 column waves x 2 K groups over 128 or 64 columns) on ragged shapes: rows
+    past M, columns past N, a last K step of 32, an odd step count (17) so
+    that one K group gets a step past the block's range.  8-wave instances
+    exist up to 5 bits and K-group instances up to 4; above, the 4-wave kernel
+    runs."""
     monkeypatch.setenv("LOWBIT_QMM_WAVES", waves)
+    monkeypatch.setenv("LOWBIT_QMM_KGROUPS", kgroups)
+    monkeypatch.setenv("LOWBIT_QMM_NT", nt)
     for (M, N, K, group, bias) in [(128, 300, 416, 32, True), (100, 520, 1024, 64, False),
-                                   (77, 257, 2080, 32, True)]:
+                                   (77, 257, 2080, 32, True), (128, 130, 2176, 128, False)]:
         run_small_linear(M, N, K, bits, group, "bf16", bias, lb.PATH_QMM, seed=bits + N)
+
+
+# (M, N, K, group, bias, blocks): LOWBIT_QMM_BLOCKS sets the block target
+# from which the schedule derives the K split (2 to 8 splits here; 0 = the
+# default target).
+SPLIT_SUM_CASES = [(128, 520, 2048, 64, True, 16), (100, 300, 4096, 128, False, 24),
+                   (77, 257, 2080, 32, True, 9), (20, 300, 1024, 32, True, 24),
+                   (128, 4096, 4096, 128, True, 0)]
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4, 5])
+def test_qmm_forced_k_splits(bits, act, monkeypatch):
+    """K splits of 2 to 8 planes, from a workspace filled with garbage: within
+    tolerance of the oracle and bitwise equal on a repeated call."""
+    monkeypatch.setenv("LOWBIT_QMM_NT", "2")    # the split counts above assume 2 column tiles
+    for (M, N, K, group, bias, blocks) in SPLIT_SUM_CASES:
+        case = Case("ss", M, K, N, bits, group, act, bias=bias, seed=bits + N + K)
+        W = weight_for(case).numpy()
+        ref = oracle.quantize(W, bits, group, act)
+        x = make_x(case)
+        b = make_bias(case)
+        y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], group, bias_values(b))
+        packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, act)
+        xd, bd = x.to(DEV), None if b is None else b.to(DEV)
+        if blocks:
+            monkeypatch.setenv("LOWBIT_QMM_BLOCKS", str(blocks))
+        need = lb.lowbit_linear_workspace_bytes(bits, group, M, N, K, TORCH_ACT[act])
+        assert need > 0, "the case must take a K split"
+        ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+        y1 = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws, path=lb.PATH_QMM)
+        y2 = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws, path=lb.PATH_QMM)
+        monkeypatch.delenv("LOWBIT_QMM_BLOCKS", raising=False)
+        torch.cuda.synchronize()
+        what = f"M={M} N={N} K={K} b={bits} g={group} {act}"
+        check_close(y1, y_ref, A, "K split " + what)
+        assert torch.equal(y1, y2), "repeated call differs: " + what
+
+
+def test_qmm_split_graph_replays():
+    """A captured MFMA call with a K split (partial planes + reduce kernel):
+    every replay, with eager work and synchronisation in between, matches the
+    eager result bit for bit."""
+    M, N, K, group, bits, act = 128, 4096, 4096, 128, 4, "bf16"
+    case = Case("gr", M, K, N, bits, group, act, bias=True, seed=7)
+    W = weight_for(case).numpy()
+    ref = oracle.quantize(W, bits, group, act)
+    packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, act)
+    xd, bd = make_x(case).to(DEV), make_bias(case).to(DEV)
+    need = lb.lowbit_linear_workspace_bytes(bits, group, M, N, K, TORCH_ACT[act])
+    assert need > 0
+    ws = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    y_eager = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            lb.lowbit_linear(xd, packed, s, z, bd, bits, group, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"graph replay {i} differs from the eager call"
+        lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws)   # eager work between
+        torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("act", ["f16", "bf16"])
