@@ -8,8 +8,15 @@ One step = one pass of the hot path over the headline workloads:
 Inputs are seeded synthetic tensors (no checkpoints), already resident in GPU
 memory when timing starts; weights are quantized and packed on the GPU before
 timing (quantization is one-off, not on the decode path).  To keep the
-256 MB Infinity Cache from serving repeated weights, every step reads a
-different copy of all weights from a rotating set of >= 1 GiB.
+256 MB Infinity Cache from serving repeated weights, every case rotates
+through its own set of weight copies of >= 1 GiB, so every launch (in the
+per-kernel loops as in the steps) reads weights that are not cached.
+
+Beside the decode timings the benchmark measures the single-launch floor of
+the device: a plain streaming read of the same byte count in one launch (the
+best of 1, 2, 4 and 8 loads per thread, over the same kind of rotation) and
+the latency of one dependent load from HBM (a pointer chase), since at a few
+MB per call launch and memory latency, not bandwidth, bound any one kernel.
 
 Printed: one JSON line.  `value` is the decode kernels' achieved algorithmic
 HBM bandwidth over bits 1..7 (sum of bytes / sum of kernel times); per-bit
@@ -41,11 +48,11 @@ ROTATE_BYTES = 1 << 30
 # kernel sources whose sha256 prefix is `src_hash`; for any other sources bench
 # reports traffic as null.
 MEASURED_TRAFFIC = {
-    "src_hash": "fd725df71bc0424b",
-    "qmv_bits1to7_bytes": 67363653,
-    "qmm_bytes": {"4096x14336": 102182115, "14336x4096": 95403274},
+    "src_hash": "cdaf4444637044b3",
+    "qmv_bits1to7_bytes": 67338632,
+    "qmm_bytes": {"4096x14336": 72839576, "14336x4096": 95391494},
     # rocprofv3 MfmaUtil (%) of the main MFMA kernel per shape
-    "qmm_mfma_util": {"4096x14336": 18.58, "14336x4096": 16.53},
+    "qmm_mfma_util": {"4096x14336": 17.46, "14336x4096": 17.68},
 }
 
 
@@ -75,6 +82,10 @@ def parse():
     ap.add_argument("--no-decode-layer", action="store_true",
                     help="skip the decoder-layer section (its q-proj launches share the kernel "
                          "and grid of the b=4 decode case, which a kernel trace would mix up)")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="skip the one-call-per-launch timing (profiling runs: only graph launches)")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the streaming-read and load-latency measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -219,6 +230,84 @@ def layer_fused(L, i, stream):
     lb.lowbit_linear_multi([item("down", 14336)], LAYER_BITS, LAYER_GROUP, stream=stream)
 
 
+def single_launch_floor(byte_counts, qmv_us, dev, stream, reps):
+    """The device's floor for one kernel that reads a few MB: a plain
+    streaming read of each byte count in one launch, rotating over >= 1 GiB
+    (graph-timed like the decode kernels; best of 1/2/4/8 loads per thread),
+    and the latency of one dependent load from HBM (pointer chase over 1 GiB
+    with links on distinct 128-byte lines, after a 1 GiB read has flushed the
+    caches)."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    buf = torch.empty(ROTATE_BYTES + (64 << 20), dtype=torch.uint8, device=dev)
+    read_us, read_lpt = [], []
+    for nb in byte_counts:
+        nb16 = (nb + 15) // 16 * 16
+        slot = (nb16 + 4095) // 4096 * 4096
+        n = max(2, ROTATE_BYTES // slot)
+        best, best_lpt = None, None
+        for lpt in (1, 2, 4, 8):
+            def fn(i, s, lpt=lpt):
+                lb.lowbit_probe_stream_read(buf[(i % n) * slot:], nb16, lpt, sink, stream=s)
+            for i in range(3):
+                fn(i, stream)
+            g = capture(fn, n, stream)
+            us = time_graph(g, max(1, reps // n + 1), n, stream)
+            del g
+            if best is None or us < best:
+                best, best_lpt = us, lpt
+        read_us.append(best)
+        read_lpt.append(best_lpt)
+    # pointer chase: links on distinct random 128-byte lines of a 1 GiB array
+    words = ROTATE_BYTES // 4
+    hops = 4096
+    gen = torch.Generator().manual_seed(5)
+    lines = torch.randperm(words // 32, generator=gen)[:hops] * 32
+    chain = torch.zeros(words, dtype=torch.int32, device=dev)
+    chain[lines.to(dev)] = torch.roll(lines, -1).to(torch.int32).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    start = int(lines[0])
+
+    def chase_us(h):
+        lb.lowbit_probe_stream_read(buf, ROTATE_BYTES, 4, sink, stream=stream)   # flush caches
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lb.lowbit_probe_chase(chain, h, start, out, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    chase_us(64)
+    lat = [(chase_us(hops) - chase_us(64)) / (hops - 64) for _ in range(3)]
+    lat_us = sorted(lat)[1]
+    del chain, buf
+    torch.cuda.empty_cache()
+    per_bit = []
+    for b, (nb, r, lpt, q) in enumerate(zip(byte_counts, read_us, read_lpt, qmv_us), start=1):
+        lower = lat_us + nb / (HBM_PEAK_GBPS * 1e3)
+        per_bit.append({"bits": b, "bytes": nb, "stream_read_us": round(r, 3),
+                        "stream_read_loads_per_thread": lpt,
+                        "stream_read_GB_s": round(nb / (r * 1e-6) / 1e9, 1),
+                        "qmv_us": round(q, 3), "qmv_over_stream_read": round(q / r, 3),
+                        "latency_plus_peak_transfer_us": round(lower, 3)})
+        log(f"floor b={b}: plain read {r:.3f} us ({lpt} loads/thread), qmv {q:.3f} us, "
+            f"latency + bytes at 8 TB/s {lower:.3f} us")
+    log(f"HBM dependent-load latency: {lat_us:.3f} us")
+    tot_read, tot_q = sum(read_us), sum(qmv_us)
+    return {"hbm_load_latency_us": round(lat_us, 3),
+            "stream_read_total_us": round(tot_read, 3),
+            "qmv_total_us": round(tot_q, 3),
+            "qmv_frac_of_stream_read": round(tot_read / tot_q, 4),
+            "stream_read_GB_s_aggregate": round(sum(byte_counts) / (tot_read * 1e-6) / 1e9, 1),
+            "by_bits": per_bit,
+            "note": "plain 16-byte streaming read of each decode case's algorithmic byte count "
+                    "in one launch (rotating over >= 1 GiB, graph-timed, best of 1/2/4/8 loads "
+                    "per thread); latency = pointer chase over 1 GiB on distinct 128-byte lines "
+                    "after a 1 GiB read; qmv_frac_of_stream_read = plain-read time / qmv time "
+                    "summed over bits 1..7"}
+
+
 def cpu_baseline(cases, reps):
     """The CPU oracle's linear (fp64 dequant + matmul) timed on this host."""
     import oracle
@@ -271,11 +360,14 @@ def main():
     qcases, mcases = qmv_cases(), qmm_cases()
     qmv_bytes_all = sum(algo_bytes(c) for c in qcases)
     qmm_bytes_all = sum(algo_bytes(c) for c in mcases)
-    copies_qmv = max(2, -(-ROTATE_BYTES // qmv_bytes_all))
-    copies_qmm = max(2, -(-ROTATE_BYTES // qmm_bytes_all))
-    log(f"preparing: qmv copies={copies_qmv}, qmm copies={copies_qmm}")
-    qp = [prepare(c, copies_qmv, dev) for c in qcases]
-    mp = [prepare(c, copies_qmm, dev) for c in mcases]
+
+    def copies_for(c):
+        return max(2, -(-ROTATE_BYTES // algo_bytes(c)))
+
+    log("preparing: weight copies per case " +
+        ", ".join(str(copies_for(c)) for c in qcases + mcases))
+    qp = [prepare(c, copies_for(c), dev) for c in qcases]
+    mp = [prepare(c, copies_for(c), dev) for c in mcases]
     torch.cuda.synchronize()
 
     def step(i, s):
@@ -288,8 +380,8 @@ def main():
         step(i, stream)
     torch.cuda.synchronize()
 
-    # One graph per rotating copy set; each holds one full step.
-    copies = min(copies_qmv, copies_qmm)
+    # One graph per rotating copy index; each holds one full step.
+    copies = min(len(p["sets"]) for p in qp + mp)
     step_graphs = [capture(lambda j, s, c=c: step(c, s), 1, stream) for c in range(copies)]
     torch.cuda.synchronize()
     for g in step_graphs:
@@ -317,7 +409,7 @@ def main():
 
     qmv_us = [kernel_us(p) for p in qp]
     qmm_us = [kernel_us(p) for p in mp]
-    eager_us = [time_eager(p, args.reps, stream) for p in qp]
+    eager_us = None if args.no_eager else [time_eager(p, args.reps, stream) for p in qp]
     per_bit = []
     for c, us in zip(qcases, qmv_us):
         gbps = algo_bytes(c) / (us * 1e-6) / 1e9
@@ -358,6 +450,10 @@ def main():
             "linear_only_us_per_token_32_layers": round(32 * fus_us, 2),
         }
 
+    floor = None
+    if not args.no_floor:
+        floor = single_launch_floor([algo_bytes(c) for c in qcases], qmv_us, dev, stream, args.reps)
+
     fresh = kernel_source_hash() == MEASURED_TRAFFIC["src_hash"]
     qmv_traffic = MEASURED_TRAFFIC["qmv_bits1to7_bytes"] if fresh else None
     qmm_traffic = (sum(MEASURED_TRAFFIC["qmm_bytes"].values()) if fresh else None)
@@ -396,6 +492,7 @@ def main():
                             + str(qmv_bytes_all),
         },
         "qmv_by_bits": per_bit,
+        "single_launch_floor": floor,
         "qmv_total_us": round(qmv_total_us, 3),
         "roofline_qmm": {
             "kernel": "qmm (M=128, bits 4, group 128, bf16)",
@@ -412,7 +509,7 @@ def main():
                               "profile of the same kernel sources; null for other sources",
         },
         "qmm": qmm,
-        "qmv_eager_us_per_call": [round(u, 3) for u in eager_us],
+        "qmv_eager_us_per_call": None if eager_us is None else [round(u, 3) for u in eager_us],
         "decode_layer": decode_layer,
         "timing": "per-kernel us = HIP-event time of replays of a HIP graph of back-to-back "
                   "launches (rotating weight copies) / launches; steps replay one graph per "

@@ -125,4 +125,13 @@ hipError_t launch_qmm_b5(const QmmParams&, const QmmLaunch&, int act, hipStream_
 hipError_t launch_qmm_b6(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b7(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 
+// ------------------------------------------------------- measurement probes --
+// Plain streaming read of `bytes` (multiple of 16) with loads_per_thread
+// (1, 2, 4 or 8) 16-byte loads per thread and round.
+hipError_t launch_stream_read(const void* src, int64_t bytes, int loads_per_thread, uint32_t* sink,
+                              hipStream_t s);
+// One lane follows `hops` dependent links of chain[0 .. chain_len) from start.
+hipError_t launch_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
+                        uint32_t* out, hipStream_t s);
+
 }  // namespace lowbit

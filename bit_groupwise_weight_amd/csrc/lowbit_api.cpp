@@ -232,9 +232,15 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   // blocks per CU, LEAN2 gains another ~10 % (4096 x 28672, 16384 x 16384;
   // at 3.5-4 blocks per CU it loses 0-3 %).  With fewer blocks the variants
   // are within 0.1 us, the default slightly ahead (K = N = 4096).
+  // Rows of more than one round per lane (K > 128 * lanes, e.g. K = 14336)
+  // also take the lean variant: b = 1/4/7 at K = 14336, N = 4096 run 3/9/11 %
+  // faster with it at two to four blocks per CU.
   const int64_t cus = device_cus();
+  bool multi_round = false;
+  for (int i = 0; i < count; ++i)
+    multi_round |= probs[i].K > (int64_t{128} << b.prob[i].lpr_shift);
   l.variant = lowbit::QMV_DEFAULT;
-  if (l.mt == 1 && total_blocks(threads, lowbit::QMV_DEFAULT) * by > 4 * cus)
+  if (l.mt == 1 && (total_blocks(threads, lowbit::QMV_DEFAULT) * by > 4 * cus || multi_round))
     l.variant = total_blocks(threads, lowbit::QMV_LEAN2) * by >= 6 * cus ? lowbit::QMV_LEAN2 : lowbit::QMV_LEAN;
   const int var_env = env_int("LOWBIT_QMV_VARIANT", -1);   // (tuning and tests: 0, 1 or 2 forces it)
   if (l.mt == 1 && var_env >= 0 && var_env <= 2) l.variant = var_env;
@@ -395,6 +401,35 @@ size_t lowbit_packed_bytes(int bits, int64_t N, int64_t K) {
 int64_t lowbit_num_groups(int64_t K, int group) {
   if (!valid_group(group) || K <= 0 || K % group != 0) return 0;
   return K / group;
+}
+
+lowbit_status lowbit_probe_stream_read(const void* src, size_t bytes, int loads_per_thread,
+                                       uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  if (!src || !sink) return fail(LOWBIT_ERR_INVALID_ARG, "NULL src or sink");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > (size_t{1} << 40))
+    return fail(LOWBIT_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (loads_per_thread != 1 && loads_per_thread != 2 && loads_per_thread != 4 && loads_per_thread != 8)
+    return fail(LOWBIT_ERR_INVALID_ARG, "loads_per_thread=%d not one of 1/2/4/8", loads_per_thread);
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(LOWBIT_ERR_MISALIGNED, "src/sink alignment");
+  const hipError_t e = lowbit::launch_stream_read(src, static_cast<int64_t>(bytes), loads_per_thread,
+                                                  sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOWBIT_OK : hip_fail(e, "stream read launch");
+}
+
+lowbit_status lowbit_probe_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
+                                 uint32_t* out, void* stream) {
+  g_last_error.clear();
+  if (!chain || !out) return fail(LOWBIT_ERR_INVALID_ARG, "NULL chain or out");
+  if (chain_len < 1 || chain_len > (int64_t{1} << 32))
+    return fail(LOWBIT_ERR_INVALID_ARG, "chain_len=%lld not in 1..2^32", (long long)chain_len);
+  if (hops < 0 || hops > (1 << 24)) return fail(LOWBIT_ERR_INVALID_ARG, "hops=%d not in 0..2^24", hops);
+  if (static_cast<int64_t>(start) >= chain_len)
+    return fail(LOWBIT_ERR_INVALID_ARG, "start=%u past the chain", start);
+  if (!aligned(chain, 4) || !aligned(out, 4)) return fail(LOWBIT_ERR_MISALIGNED, "chain/out alignment");
+  const hipError_t e = lowbit::launch_chase(chain, chain_len, hops, start, out,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOWBIT_OK : hip_fail(e, "chase launch");
 }
 
 const char* lowbit_status_string(lowbit_status s) {

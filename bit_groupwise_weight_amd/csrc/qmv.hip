@@ -243,7 +243,15 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
       run_coords(rr, m, ul, j);
       const int k = (rbase + ul + lanes * j) * 32;
       const bool valid = rr < nruns && m < mcount && k < p.K;
-      load_raw_run<ACT>(p.x, valid ? static_cast<int64_t>(m0 + m) * p.K + k : 0, raw);
+      // (threads without a real run load nothing: at one activation row
+      // they are half the block, and their loads would add half again to the
+      // block's activation traffic)
+      if (valid) {
+        load_raw_run<ACT>(p.x, static_cast<int64_t>(m0 + m) * p.K + k, raw);
+      } else {
+#pragma unroll
+        for (int i = 0; i < RAW; ++i) raw[i] = 0u;
+      }
       return valid;
     };
     uint32_t raw[RAW];

@@ -31,7 +31,7 @@ _ENUM_DTYPE = {v: k for k, v in _DTYPE_ENUM.items()}
 EXPORTED_SYMBOLS = (
     "lowbit_abi_version", "lowbit_packed_bytes", "lowbit_num_groups", "lowbit_quantize_pack",
     "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path", "lowbit_linear_multi",
-    "lowbit_status_string", "lowbit_last_error",
+    "lowbit_status_string", "lowbit_last_error", "lowbit_probe_stream_read", "lowbit_probe_chase",
 )
 MAX_MULTI = 8   # LOWBIT_MAX_MULTI
 
@@ -93,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_last_error.restype = ctypes.c_char_p
     lib.lowbit_last_error.argtypes = []
+    lib.lowbit_probe_stream_read.restype = ctypes.c_int
+    lib.lowbit_probe_stream_read.argtypes = [vp, c_sz, ctypes.c_int, vp, vp]
+    lib.lowbit_probe_chase.restype = ctypes.c_int
+    lib.lowbit_probe_chase.argtypes = [vp, c_i64, ctypes.c_int, ctypes.c_uint32, vp, vp]
     _lib = lib
     return lib
 
@@ -321,3 +325,34 @@ def lowbit_linear_multi(items, bits: int, group: int, stream=None):
                                      _stream_handle(x0.device, stream))
     _check(st, "lowbit_linear_multi")
     return outs
+
+
+# ---------------------------------------------------------------- probes --
+# Measurement instruments of the library (not part of the layer): a plain
+# streaming read and a dependent-load chain, used by the benchmark to report
+# the decode kernel against the single-launch floor of the device.
+
+def lowbit_probe_stream_read(src: torch.Tensor, nbytes: int, loads_per_thread: int,
+                             sink: torch.Tensor, stream=None) -> None:
+    """Read the first nbytes of src (device) with plain 16-byte loads in one launch."""
+    lib = load()
+    _require_cuda(src, sink)
+    _expect(nbytes <= src.numel() * src.element_size(), "nbytes exceeds src")
+    _expect(sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1, "sink: one 32-bit word")
+    with torch.cuda.device(src.device):
+        st = lib.lowbit_probe_stream_read(_ptr(src), nbytes, loads_per_thread, _ptr(sink),
+                                          _stream_handle(src.device, stream))
+    _check(st, "lowbit_probe_stream_read")
+
+
+def lowbit_probe_chase(chain: torch.Tensor, hops: int, start: int, out: torch.Tensor,
+                       stream=None) -> None:
+    """Follow hops dependent links i <- chain[i] (int32/uint32 device array) from start."""
+    lib = load()
+    _require_cuda(chain, out)
+    _expect(chain.dtype in (torch.int32, torch.uint32) and chain.is_contiguous(), "chain: 32-bit, contiguous")
+    _expect(out.dtype in (torch.int32, torch.uint32) and out.numel() >= 1, "out: one 32-bit word")
+    with torch.cuda.device(chain.device):
+        st = lib.lowbit_probe_chase(_ptr(chain), chain.numel(), hops, start, _ptr(out),
+                                    _stream_handle(chain.device, stream))
+    _check(st, "lowbit_probe_chase")

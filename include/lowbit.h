@@ -190,6 +190,29 @@ typedef struct lowbit_linear_desc {
 lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lowbit_dtype act_dtype,
                                   int bits, int group, int64_t M, void* stream);
 
+/* ---- Measurement instruments (not part of the layer) ----
+ * The decode kernel reads a few MB per call, where launch and memory latency
+ * rather than bandwidth bound any single kernel.  These two calls measure
+ * that floor on the running device so a benchmark can report the decode
+ * kernel against it.
+ *
+ * lowbit_probe_stream_read: reads `bytes` (a positive multiple of 16, src
+ * 16-byte aligned) from device memory with plain 16-byte loads,
+ * loads_per_thread (1, 2, 4 or 8) per thread per round, in one launch of
+ * 256-thread blocks, and discards the data (`sink`, one device word, is
+ * written only if the data fold to a fixed constant).  Enqueued on `stream`.
+ *
+ * lowbit_probe_chase: one lane follows `hops` (0 .. 2^24) dependent links
+ * i <- chain[i] of the device array chain[0 .. chain_len) from index
+ * `start`, each link clamped to chain_len - 1 (any contents are safe), and
+ * writes the final index to the device word `out`.  With links that point
+ * to distinct cache lines outside every cache, the time per hop is the
+ * latency of one load from HBM.  Enqueued on `stream`. */
+lowbit_status lowbit_probe_stream_read(const void* src, size_t bytes, int loads_per_thread,
+                                       uint32_t* sink, void* stream);
+lowbit_status lowbit_probe_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
+                                 uint32_t* out, void* stream);
+
 /* Static text for a status code. */
 const char* lowbit_status_string(lowbit_status status);
 

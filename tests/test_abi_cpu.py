@@ -135,3 +135,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("LOWBIT_LIBRARY", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         lb.load()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1024, 4, A), INVALID), ((A, 1024, 4, None), INVALID), ((A, 0, 4, A), INVALID),
+    ((A, 1000, 4, A), INVALID), ((A, 1024, 3, A), INVALID), ((A + 8, 1024, 4, A), MISALIGNED),
+    ((A, 1024, 4, A + 2), MISALIGNED)])
+def test_probe_stream_read_validation(lowbit_lib, args, status):
+    assert lowbit_lib.lowbit_probe_stream_read(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 16, 4, 0, A), INVALID), ((A, 16, 4, 0, None), INVALID), ((A, 0, 4, 0, A), INVALID),
+    ((A, 16, -1, 0, A), INVALID), ((A, 16, (1 << 24) + 1, 0, A), INVALID), ((A, 16, 4, 16, A), INVALID),
+    ((A + 2, 16, 4, 0, A), MISALIGNED), ((A, 16, 4, 0, A + 1), MISALIGNED)])
+def test_probe_chase_validation(lowbit_lib, args, status):
+    assert lowbit_lib.lowbit_probe_chase(*args, None) == status
