@@ -142,7 +142,7 @@ const QmvStageBytes kQmvStage[8] = {nullptr,
                                     lowbit::qmv_stage_bytes_b7};
 
 // LDS budget of one decode block for its staged activations.
-constexpr int64_t kQmvStageBudget = 64 * 1024 - 256;  // minus one scratch run
+constexpr int64_t kQmvStageBudget = 64 * 1024 - 256;
 
 int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -226,12 +226,13 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   }
   if (threads < (1 << max_shift)) threads = 1 << max_shift;
   const int64_t by = (M + l.mt - 1) / l.mt;
-  // One activation row: with more than four blocks per CU the lean variant
+  // One activation row: with more than two blocks per CU the lean variant
   // (one more wave per SIMD) gains 7-9 % at b = 4 from 4096 x 14336 to
-  // 16384 x 16384, and where two rows per lane group still leave six or more
-  // blocks per CU, LEAN2 gains another ~10 % (4096 x 28672, 16384 x 16384;
-  // at 3.5-4 blocks per CU it loses 0-3 %).  With fewer blocks the variants
-  // are within 0.1 us, the default slightly ahead (K = N = 4096).
+  // 16384 x 16384 and 12 % at b = 1, 4096 x 14336 (3.5 blocks per CU), and
+  // where two rows per lane group still leave six or more blocks per CU,
+  // LEAN2 gains another ~10 % (4096 x 28672, 16384 x 16384; at 3.5-4 blocks
+  // per CU it loses 0-3 %).  With two blocks per CU or fewer the default is
+  // ahead by 0-3 % (K = N = 4096).
   // Rows of more than one round per lane (K > 128 * lanes, e.g. K = 14336)
   // also take the lean variant: b = 1/4/7 at K = 14336, N = 4096 run 3/9/11 %
   // faster with it at two to four blocks per CU.
@@ -240,7 +241,7 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   for (int i = 0; i < count; ++i)
     multi_round |= probs[i].K > (int64_t{128} << b.prob[i].lpr_shift);
   l.variant = lowbit::QMV_DEFAULT;
-  if (l.mt == 1 && (total_blocks(threads, lowbit::QMV_DEFAULT) * by > 4 * cus || multi_round))
+  if (l.mt == 1 && (total_blocks(threads, lowbit::QMV_DEFAULT) * by > 2 * cus || multi_round))
     l.variant = total_blocks(threads, lowbit::QMV_LEAN2) * by >= 6 * cus ? lowbit::QMV_LEAN2 : lowbit::QMV_LEAN;
   const int var_env = env_int("LOWBIT_QMV_VARIANT", -1);   // (tuning and tests: 0, 1 or 2 forces it)
   if (l.mt == 1 && var_env >= 0 && var_env <= 2) l.variant = var_env;

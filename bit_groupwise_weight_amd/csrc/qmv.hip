@@ -288,9 +288,8 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
     // -- stage the round's activations: layout [m][j][quad][lane-in-group].
     // The thread's first run (loaded above, before the weights) is staged
     // outside the loop so that only the activation loads must have landed.
-    // (Threads without a run write to a scratch slot past the stage, which
-    // keeps this code unconditional so the compiler cannot sink the
-    // activation loads behind the weight loads.)
+    // Threads without a run (past nruns: at one activation row, half the
+    // block) skip the staging arithmetic; runs past M or K stage zeros.
     auto stage_store = [&](int rr, bool valid) {
       int m, ul, j;
       run_coords(rr, m, ul, j);
@@ -298,13 +297,12 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
       for (int i = 0; i < RAW; ++i) raw[i] = valid ? raw[i] : 0u;
       uint32_t out[QD * 4];
       stage_run<ACT, BITS>(raw, out);
-      const bool real = rr < nruns;
 #pragma unroll
       for (int q = 0; q < QD; ++q)
-        stage[real ? ((m * 4 + j) * QD + q) * lanes + ul : nruns * QD + q] =
+        stage[((m * 4 + j) * QD + q) * lanes + ul] =
             make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
     };
-    stage_store(tid, raw_valid);
+    if (tid < nruns) stage_store(tid, raw_valid);
     for (int rr = tid + blockDim.x; rr < nruns; rr += blockDim.x) {
       const bool v = run_load(rr, raw);
       stage_store(rr, v);
@@ -389,12 +387,10 @@ __global__ __launch_bounds__(256) void qmv_multi_kernel(QmvBatch b) {
 
 template <int GROUP, int ACT, int MT, int VAR>
 static hipError_t launch_one(const QmvBatch& b, const QmvLaunch& l, hipStream_t s) {
-  // staged runs (sized for the widest lane group) plus one scratch run for
-  // threads without a run
+  // staged runs (sized for the widest lane group)
   int shift = 0;
   for (unsigned i = 0; i < l.grid.z; ++i) shift = b.prob[i].lpr_shift > shift ? b.prob[i].lpr_shift : shift;
-  const size_t lds = (static_cast<size_t>(MT) * 4 * (size_t(1) << shift) + 1) *
-                     RunQuads<ACT, LOWBIT_BITS>::n * 16;
+  const size_t lds = static_cast<size_t>(MT) * 4 * (size_t(1) << shift) * RunQuads<ACT, LOWBIT_BITS>::n * 16;
   if (l.grid.z == 1)
     qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, VAR><<<l.grid, l.block, lds, s>>>(b.prob[0]);
   else
