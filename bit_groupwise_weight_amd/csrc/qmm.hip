@@ -519,20 +519,17 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams p, QmmReduceS
   const int m = (by << (4 + r.mtt_shift)) + (mt << 4) + 4 * (lane >> 4);
   if (n >= p.N || m >= p.M) return;
   const float4_t* src = reinterpret_cast<const float4_t*>(p.partials) + q;
-  // planes are read sixteen at a time (loads past the last plane predicated
-  // off) so that all their loads are in flight together; the sum stays in
-  // plane order
-  constexpr int PB = 16;
+  // planes are read four at a time so that their loads are in flight together
   float4_t v = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < r.splits; z += PB) {
-    float4_t t[PB];
+  int z = 0;
+  for (; z + 4 <= r.splits; z += 4) {
+    float4_t t[4];
 #pragma unroll
-    for (int u = 0; u < PB; ++u)
-      if (z + u < r.splits) t[u] = src[(z + u) * r.plane_recs];
+    for (int u = 0; u < 4; ++u) t[u] = src[(z + u) * r.plane_recs];
 #pragma unroll
-    for (int u = 0; u < PB; ++u)
-      if (z + u < r.splits) v += t[u];
+    for (int u = 0; u < 4; ++u) v += t[u];
   }
+  for (; z < r.splits; ++z) v += src[z * r.plane_recs];
   const float b = p.bias ? load_act<ACT>(p.bias, n) : 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
