@@ -42,12 +42,13 @@ struct QmvParams {
 // bytes in flight per wave).
 enum QmvVariant { QMV_DEFAULT = 0, QMV_LEAN = 1, QMV_LEAN2 = 2 };
 // Rows per row group of the decode kernel for one activation row per pass:
-// two rows for 1, 2, 3 and 5-bit codes, one for 4, 6 and 7 bits (measured on
-// MI355X at K = N = 4096: each choice is 0.1-0.5 us faster than the other
-// there), two for every width in LEAN2; one row whenever several activation
-// rows share a pass.
+// two rows for 1, 2 and 3-bit codes, one for 4..7 bits (measured on MI355X at
+// K = N = 4096, A/B of both builds on one box: two rows 0.15-0.18 us faster
+// at b = 1, 2, equal at b = 3, 4, 6, 7, one row 0.35 us faster at b = 5),
+// two for every width in LEAN2; one row whenever several activation rows
+// share a pass.
 constexpr int qmv_rows_per_group(int bits, int mt, int variant) {
-  return mt == 1 && (variant == QMV_LEAN2 || bits <= 3 || bits == 5) ? 2 : 1;
+  return mt == 1 && (variant == QMV_LEAN2 || bits <= 3) ? 2 : 1;
 }
 // Up to kQmvMaxProblems decode problems of one bit width, group size and
 // activation dtype served by one launch: blocks with blockIdx.z == i work on
