@@ -318,37 +318,52 @@ void qmm_split(QmmSchedule& sc, int64_t M, int64_t N, int64_t K) {
 // K = 14336 36.0 vs 33.3).
 constexpr int kQmmNarrowMaxSteps = 16;
 
+// Two K groups need enough steps per block for their two-step pipeline:
+// measured (A/B in alternating processes on one box) K groups win with 14-16
+// steps per block (M = 128, K = 14336, N = 4096: 34.2 vs 35.0 us; M = 64,
+// K = 4096, N = 14336: 30.8 vs 33.1; M = 32: 27.1 vs 28.4) and lose with 4
+// (M = 64, K = N = 4096: 17.25 vs 16.8).
+constexpr int kQmmKGroupsMinSteps = 8;
+
 QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   const int mtt_env = env_int("LOWBIT_QMM_MTT", 0);
   if (mtt_env == 1 || mtt_env == 2 || mtt_env == 4 || mtt_env == 8) sc.mtt = std::min(sc.mtt, mtt_env);
   sc.nt = 2;
-  // Two waves per SIMD (8-wave blocks, 256 columns) for full 128-row tiles
-  // when N is wide enough that the K split stays small: one wave's
-  // dequantization then runs under the other's MFMAs (measured 1.6x more work
-  // per CU than 4-wave blocks at M = 128, K = 4096, N = 14336), but the wider
-  // tile needs twice the K splits, whose partial planes cost more than that
-  // gain once the split exceeds ~4 (N = 4096 is faster with 4-wave blocks).
   // Two K groups of 4 column waves (8 waves, 128 columns) keep two waves per
   // SIMD at the tile width of a 4-wave block, so the K split across blocks
-  // stays that of the 4-wave block; used for full 128-row tiles up to 4 bits.
+  // stays that of the 4-wave block: one wave's dequantization runs under the
+  // other's MFMAs.  Up to 4 bits, with at least kQmmKGroupsMinSteps steps per
+  // block; 128-row tiles may narrow to one column tile per wave (below).
+  // Otherwise one K group: 8 column waves (256 columns) for full 128-row
+  // tiles when N is wide enough that the K split stays small (1.6x more work
+  // per CU than 4-wave blocks at M = 128, K = 4096, N = 14336; the wider tile
+  // needs twice the K splits, whose partial planes cost more than that gain
+  // once the split exceeds ~4), else 4 waves.
   // (LOWBIT_QMM_MTT, LOWBIT_QMM_KGROUPS, LOWBIT_QMM_WAVES and LOWBIT_QMM_NT
   // override the choices for tuning; LOWBIT_QMM_WAVES applies with one K
-  // group, LOWBIT_QMM_NT with two.)
+  // group, LOWBIT_QMM_NT with two at 128-row tiles.)
   const bool can8 = bits <= lowbit::qmm_max_bits_8waves;
   const bool can_kg = bits <= lowbit::qmm_max_bits_kgroups;
-  const int kg_default = (can_kg && sc.mtt == 8) ? 2 : 1;
-  sc.kgroups = (can_kg && env_int("LOWBIT_QMM_KGROUPS", kg_default) == 2) ? 2 : 1;
-  const int wv_default = (can8 && sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
-  sc.waves = sc.kgroups == 2 ? 4 : (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
-  if (sc.kgroups == 2 && sc.mtt == 8) {
-    QmmSchedule narrow = sc;
-    narrow.nt = 1;
-    qmm_split(narrow, M, N, K);
-    const int nt_env = env_int("LOWBIT_QMM_NT", 0);
-    if (nt_env == 1 || (nt_env != 2 && narrow.ksteps_per_split <= kQmmNarrowMaxSteps)) return narrow;
+  const int kg_env = env_int("LOWBIT_QMM_KGROUPS", 0);
+  if (can_kg && kg_env != 1) {
+    QmmSchedule kg = sc;
+    kg.kgroups = 2;
+    kg.waves = 4;
+    if (kg.mtt == 8) {
+      QmmSchedule narrow = kg;
+      narrow.nt = 1;
+      qmm_split(narrow, M, N, K);
+      const int nt_env = env_int("LOWBIT_QMM_NT", 0);
+      if (nt_env == 1 || (nt_env != 2 && narrow.ksteps_per_split <= kQmmNarrowMaxSteps)) return narrow;
+    }
+    qmm_split(kg, M, N, K);
+    if (kg_env == 2 || kg.ksteps_per_split >= kQmmKGroupsMinSteps) return kg;
   }
+  sc.kgroups = 1;
+  const int wv_default = (can8 && sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
+  sc.waves = (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
   qmm_split(sc, M, N, K);
   return sc;
 }
