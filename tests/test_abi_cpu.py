@@ -151,3 +151,20 @@ def test_probe_stream_read_validation(lowbit_lib, args, status):
     ((A + 2, 16, 4, 0, A), MISALIGNED), ((A, 16, 4, 0, A + 1), MISALIGNED)])
 def test_probe_chase_validation(lowbit_lib, args, status):
     assert lowbit_lib.lowbit_probe_chase(*args, None) == status
+
+
+@pytest.mark.parametrize("M,K,N,bits,group,dtype,planes", [
+    (128, 4096, 14336, 4, 128, "bf16", 2),    # two K groups, 112 tiles, split in 2
+    (128, 14336, 4096, 4, 128, "bf16", 8),    # two K groups, 32 tiles, split in 8
+    (128, 1024, 14336, 4, 128, "bf16", 0),    # short loop: 64-column tiles, no split
+    (64, 4096, 4096, 4, 64, "f16", 8),        # 4 steps per block: one K group
+    (64, 4096, 14336, 4, 64, "f16", 2),       # 16 steps per block: two K groups
+    (128, 4096, 14336, 7, 128, "bf16", 2),    # 7 bits: 4-wave blocks
+    (16, 4096, 4096, 4, 64, "f16", 8),
+])
+def test_mfma_schedule_workspace(lowbit_lib, M, K, N, bits, group, dtype, planes):
+    """The MFMA schedule on a 256-CU device, seen through the workspace it asks
+    for: one fp32 M x N plane per K split (none without a split)."""
+    import torch
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    assert lb.lowbit_linear_workspace_bytes(bits, group, M, N, K, dt) == planes * M * N * 4
