@@ -36,7 +36,7 @@ struct QmvParams {
   int64_t row_bytes;      // K * bits / 8
 };
 // Variants of the decode kernel for one activation row per pass (chosen at
-// launch from the blocks per CU): the default; LEAN, which keeps one staged
+// launch from the blocks per CU and the row length): the default; LEAN, which keeps one staged
 // fragment live at a time (fewer registers, one more wave per SIMD); and
 // LEAN2, LEAN with two rows per lane group at every bit width (more weight
 // bytes in flight per wave).

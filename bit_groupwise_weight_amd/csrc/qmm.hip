@@ -6,8 +6,9 @@
 // int4 weight-only decode falling far behind -- the batched path matters.
 //
 // Layout on CDNA4 (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation):
-//   * block tile: 16*MTT rows (M) x 32*WV columns (N); WV = 4 or 8 waves,
-//     wave w owns two 16-wide column tiles and all M rows; one block per CU;
+//   * block tile: 16*MTT rows (M) x 16*NT*WC columns (N); WC column waves
+//     (4 or 8), column wave c owns NT (2, or 1 for narrow tiles) 16-wide
+//     column tiles and all M rows; one block per CU;
 //   * K advances in steps of 128.  Within a step, lane group g = lane/16 owns
 //     the 32 consecutive K positions [32g, 32g+32); MFMA slot 8g+t of k-sub
 //     ks (0..3) is K position 32g + 8ks + t for both operands, so each lane's
@@ -18,10 +19,10 @@
 //     column belongs to exactly one wave, so no LDS round trip is needed;
 //     4-bit codes are split into even / odd byte planes so that each code
 //     converts straight from a byte;
-//   * the activation tile (16*MTT x 128) is shared by the 4 waves through
-//     two LDS stages (rows swizzled by XOR); it is loaded into registers two
-//     steps ahead and stored into the next stage while the current one is
-//     read;
+//   * the activation tile (16*MTT x 128) is shared by the waves through two
+//     LDS stages (rows swizzled by XOR); it is loaded into registers two
+//     steps ahead (one with two K groups) and stored into the next stage
+//     while the current one is read;
 //   * codes are loaded two steps ahead; the MFMAs of each k-sub are issued
 //     in a fixed order with the dequantization of the next k-sub spread
 //     between them;
