@@ -36,19 +36,21 @@ struct QmvParams {
   int64_t row_bytes;      // K * bits / 8
 };
 // Variants of the decode kernel for one activation row per pass (chosen at
-// launch from the blocks per CU and the row length): the default; LEAN, which keeps one staged
-// fragment live at a time (fewer registers, one more wave per SIMD); and
-// LEAN2, LEAN with two rows per lane group at every bit width (more weight
-// bytes in flight per wave).
-enum QmvVariant { QMV_DEFAULT = 0, QMV_LEAN = 1, QMV_LEAN2 = 2 };
+// launch from the blocks per CU, the waves per CU and the row length): the
+// default; LEAN, which keeps one staged fragment live at a time (fewer
+// registers, one more wave per SIMD); LEAN2, LEAN with two rows per lane
+// group at every bit width (more weight bytes in flight per wave); and LEAN1,
+// LEAN with one row per lane group at every bit width (twice the waves where
+// the default has two rows, for launches too small to fill the CUs).
+enum QmvVariant { QMV_DEFAULT = 0, QMV_LEAN = 1, QMV_LEAN2 = 2, QMV_LEAN1 = 3 };
 // Rows per row group of the decode kernel for one activation row per pass:
 // two rows for 1, 2 and 3-bit codes, one for 4..7 bits (measured on MI355X at
 // K = N = 4096, A/B of both builds on one box: two rows 0.15-0.18 us faster
 // at b = 1, 2, equal at b = 3, 4, 6, 7, one row 0.35 us faster at b = 5),
-// two for every width in LEAN2; one row whenever several activation rows
-// share a pass.
+// two for every width in LEAN2, one in LEAN1; one row whenever several
+// activation rows share a pass.
 constexpr int qmv_rows_per_group(int bits, int mt, int variant) {
-  return mt == 1 && (variant == QMV_LEAN2 || bits <= 3) ? 2 : 1;
+  return mt == 1 && variant != QMV_LEAN1 && (variant == QMV_LEAN2 || bits <= 3) ? 2 : 1;
 }
 // Up to kQmvMaxProblems decode problems of one bit width, group size and
 // activation dtype served by one launch: blocks with blockIdx.z == i work on

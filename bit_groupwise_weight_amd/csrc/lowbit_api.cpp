@@ -240,11 +240,19 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   bool multi_round = false;
   for (int i = 0; i < count; ++i)
     multi_round |= probs[i].K > (int64_t{128} << b.prob[i].lpr_shift);
+  // Launches too small to give every CU two waves (e.g. N = 1024 at 1-3
+  // bits, two rows per lane group: one wave per CU) take one row per lane
+  // group, which doubles the waves (A/B on one box: K = 4096, N = 1024, b = 1,
+  // 2, 3: 3.81/3.96/4.09 -> 3.59/3.67/3.77 us; K = 2048, N = 1024, b = 1, 3:
+  // 3.12/3.47 -> 2.71/3.10 us; at two waves per CU, N = 2048, it loses 3-4 %).
   l.variant = lowbit::QMV_DEFAULT;
+  const int64_t waves = total_blocks(threads, lowbit::QMV_DEFAULT) * by * (threads / 64);
   if (l.mt == 1 && (total_blocks(threads, lowbit::QMV_DEFAULT) * by > 2 * cus || multi_round))
     l.variant = total_blocks(threads, lowbit::QMV_LEAN2) * by >= 6 * cus ? lowbit::QMV_LEAN2 : lowbit::QMV_LEAN;
-  const int var_env = env_int("LOWBIT_QMV_VARIANT", -1);   // (tuning and tests: 0, 1 or 2 forces it)
-  if (l.mt == 1 && var_env >= 0 && var_env <= 2) l.variant = var_env;
+  else if (l.mt == 1 && waves < 2 * cus && lowbit::qmv_rows_per_group(bits, 1, lowbit::QMV_DEFAULT) == 2)
+    l.variant = lowbit::QMV_LEAN1;
+  const int var_env = env_int("LOWBIT_QMV_VARIANT", -1);   // (tuning and tests: 0..3 forces it)
+  if (l.mt == 1 && var_env >= 0 && var_env <= 3) l.variant = var_env;
   int64_t bx = 0;
   for (int i = 0; i < count; ++i) bx = std::max<int64_t>(bx, blocks_for(threads, i, l.variant));
   if (bx > 0x7fffffff || by > 65535) return fail(LOWBIT_ERR_INVALID_ARG, "problem too large");

@@ -402,9 +402,12 @@ template <int GROUP, int ACT>
 static hipError_t dispatch_mt(const QmvBatch& p, const QmvLaunch& l, hipStream_t s) {
   switch (l.mt) {
     case 1:
-      // (LEAN2 is LEAN where the default already has two rows per group)
+      // (LEAN2 is LEAN where the default already has two rows per group,
+      // LEAN1 is LEAN where it has one)
       if (l.variant == QMV_LEAN2 && qmv_rows_per_group(LOWBIT_BITS, 1, QMV_DEFAULT) == 1)
         return launch_one<GROUP, ACT, 1, QMV_LEAN2>(p, l, s);
+      if (l.variant == QMV_LEAN1 && qmv_rows_per_group(LOWBIT_BITS, 1, QMV_DEFAULT) == 2)
+        return launch_one<GROUP, ACT, 1, QMV_LEAN1>(p, l, s);
       if (l.variant != QMV_DEFAULT) return launch_one<GROUP, ACT, 1, QMV_LEAN>(p, l, s);
       return launch_one<GROUP, ACT, 1, QMV_DEFAULT>(p, l, s);
     case 2: return launch_one<GROUP, ACT, 2, QMV_LEAN>(p, l, s);

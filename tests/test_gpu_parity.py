@@ -171,8 +171,8 @@ def test_qmm_small(bits, act):
 @pytest.mark.parametrize("bits", range(1, 8))
 def test_qmv_register_variants(bits, act, monkeypatch):
     """The decode-kernel variants for one activation row (the default, the
-    register-lean one and the lean one with two rows per lane group, chosen
-    by blocks per CU) on ragged shapes: each matches the oracle, and all
+    register-lean one, and the lean ones with two or one rows per lane group,
+    chosen by blocks and waves per CU) on ragged shapes: each matches the oracle, and all
     agree bit for bit (they differ in register use and in which rows share a
     lane group, not in the arithmetic of a row)."""
     for (N, K, group, bias) in [(200, 384, 64, True), (67, 352, 32, False), (130, 1024, 256, True)]:
@@ -183,7 +183,7 @@ def test_qmv_register_variants(bits, act, monkeypatch):
         y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], group, bias_values(b))
         packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, act)
         outs = []
-        for variant in ("0", "1", "2"):
+        for variant in ("0", "1", "2", "3"):
             monkeypatch.setenv("LOWBIT_QMV_VARIANT", variant)
             y = lb.lowbit_linear(x.to(DEV), packed, s, z, None if b is None else b.to(DEV), bits, group,
                                  path=lb.PATH_QMV)
