@@ -121,30 +121,59 @@ __device__ __forceinline__ float ubyte(uint32_t v) {  // v_cvt_f32_ubyte<I>
   return static_cast<float>((v >> (8 * I)) & 0xFFu);
 }
 
+// Scale and zero of one 32-code run: as fp32 values, and (fp16 activations)
+// as packed pairs of the fp16 bits, (s, s) and (z, z).
+struct ScaleZero {
+  float s, z;
+  uint32_t s2, z2;
+};
+
 // Dequantize codes I and I+1 of a 32-code run into one packed pair.
 template <int BITS, int ACT, int I>
-__device__ __forceinline__ uint32_t dequant2(const uint32_t* w, float s, float z) {
-  const float a = __builtin_fmaf(s, static_cast<float>(code_at<BITS, I>(w)), z);
-  const float b = __builtin_fmaf(s, static_cast<float>(code_at<BITS, I + 1>(w)), z);
+__device__ __forceinline__ uint32_t dequant2(const uint32_t* w, const ScaleZero& sz) {
+  const float a = __builtin_fmaf(sz.s, static_cast<float>(code_at<BITS, I>(w)), sz.z);
+  const float b = __builtin_fmaf(sz.s, static_cast<float>(code_at<BITS, I + 1>(w)), sz.z);
   return pack2<ACT>(a, b);
+}
+
+// fp16 activations, 4-bit codes: byte J of the even-code plane `lo` and of
+// the odd-code plane `hi` become one packed pair in packed fp16 arithmetic.
+// With the exponent field of 1024 OR-ed above it, a code q in the low bits
+// of a half reads as the fp16 value 1024 + q; subtracting 1024 is exact, and
+// one packed FMA gives s*q + z rounded once to fp16 (the fp32 path rounds
+// s*q + z to fp32 first, then to fp16).
+template <int J>
+__device__ __forceinline__ uint32_t dq_pair_f16_b4(uint32_t lo, uint32_t hi, const ScaleZero& sz) {
+  // byte 0 = lo byte J, byte 2 = hi byte J, bytes 1 and 3 = 0
+  constexpr uint32_t sel = J | (0x0Cu << 8) | ((4u + J) << 16) | (0x0Cu << 24);
+  const uint32_t v = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+  const half2v_t q = __builtin_bit_cast(half2v_t, v) - half2v_t{1024, 1024};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, __builtin_bit_cast(half2v_t, sz.s2),
+                                                                __builtin_bit_cast(half2v_t, sz.z2)));
 }
 
 // Dequantize k-sub KS (codes [8KS, 8KS+8)) of a 32-code run into one MFMA
 // operand: four packed pairs (code 8KS+2j in the low half of dword j).
 template <int BITS, int ACT, int KS>
-__device__ __forceinline__ uint4 dequant_ksub(const uint32_t (&w)[BITS], float s, float z) {
+__device__ __forceinline__ uint4 dequant_ksub(const uint32_t (&w)[BITS], const ScaleZero& sz) {
   if constexpr (BITS == 4) {
     // word KS holds the 8 codes as nibbles: split them into two byte planes
     // (even codes, odd codes) so that every code converts straight from a byte
     const uint32_t lo = and_nibbles(w[KS]);
     const uint32_t hi = and_nibbles(w[KS] >> 4);
-    return make_uint4(pack2<ACT>(__builtin_fmaf(s, ubyte<0>(lo), z), __builtin_fmaf(s, ubyte<0>(hi), z)),
-                      pack2<ACT>(__builtin_fmaf(s, ubyte<1>(lo), z), __builtin_fmaf(s, ubyte<1>(hi), z)),
-                      pack2<ACT>(__builtin_fmaf(s, ubyte<2>(lo), z), __builtin_fmaf(s, ubyte<2>(hi), z)),
-                      pack2<ACT>(__builtin_fmaf(s, ubyte<3>(lo), z), __builtin_fmaf(s, ubyte<3>(hi), z)));
+    if constexpr (ACT == ACT_F16) {
+      return make_uint4(dq_pair_f16_b4<0>(lo, hi, sz), dq_pair_f16_b4<1>(lo, hi, sz),
+                        dq_pair_f16_b4<2>(lo, hi, sz), dq_pair_f16_b4<3>(lo, hi, sz));
+    } else {
+      const float s = sz.s, z = sz.z;
+      return make_uint4(pack2<ACT>(__builtin_fmaf(s, ubyte<0>(lo), z), __builtin_fmaf(s, ubyte<0>(hi), z)),
+                        pack2<ACT>(__builtin_fmaf(s, ubyte<1>(lo), z), __builtin_fmaf(s, ubyte<1>(hi), z)),
+                        pack2<ACT>(__builtin_fmaf(s, ubyte<2>(lo), z), __builtin_fmaf(s, ubyte<2>(hi), z)),
+                        pack2<ACT>(__builtin_fmaf(s, ubyte<3>(lo), z), __builtin_fmaf(s, ubyte<3>(hi), z)));
+    }
   } else {
-    return make_uint4(dequant2<BITS, ACT, 8 * KS + 0>(w, s, z), dequant2<BITS, ACT, 8 * KS + 2>(w, s, z),
-                      dequant2<BITS, ACT, 8 * KS + 4>(w, s, z), dequant2<BITS, ACT, 8 * KS + 6>(w, s, z));
+    return make_uint4(dequant2<BITS, ACT, 8 * KS + 0>(w, sz), dequant2<BITS, ACT, 8 * KS + 2>(w, sz),
+                      dequant2<BITS, ACT, 8 * KS + 4>(w, sz), dequant2<BITS, ACT, 8 * KS + 6>(w, sz));
   }
 }
 
@@ -159,12 +188,14 @@ __device__ __forceinline__ int stage_swizzle(int r) { return ((r & 3) << 2) | ((
 // into one operand dword.  For 4-bit codes, lo / hi are the byte planes of
 // word KS (even codes, odd codes), so every code converts straight from a byte.
 template <int BITS, int ACT, int KS, int J>
-__device__ __forceinline__ uint32_t dq_pair(const uint32_t (&w)[BITS], uint32_t lo, uint32_t hi, float s,
-                                            float z) {
-  if constexpr (BITS == 4) {
-    return pack2<ACT>(__builtin_fmaf(s, ubyte<J>(lo), z), __builtin_fmaf(s, ubyte<J>(hi), z));
+__device__ __forceinline__ uint32_t dq_pair(const uint32_t (&w)[BITS], uint32_t lo, uint32_t hi,
+                                            const ScaleZero& sz) {
+  if constexpr (BITS == 4 && ACT == ACT_F16) {
+    return dq_pair_f16_b4<J>(lo, hi, sz);
+  } else if constexpr (BITS == 4) {
+    return pack2<ACT>(__builtin_fmaf(sz.s, ubyte<J>(lo), sz.z), __builtin_fmaf(sz.s, ubyte<J>(hi), sz.z));
   } else {
-    return dequant2<BITS, ACT, 8 * KS + 2 * J>(w, s, z);
+    return dequant2<BITS, ACT, 8 * KS + 2 * J>(w, sz);
   }
 }
 
@@ -251,12 +282,18 @@ __global__ __launch_bounds__(64 * WC * KGR, 1) void qmm_kernel(QmmParams p) {
       c.z[nt] = ze_bits[gi];
     }
   };
-  auto scale_zero = [&](const Codes& c, float (&sv)[NT], float (&zv)[NT]) {
+  auto scale_zero = [&](const Codes& c, ScaleZero (&sz)[NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint32_t ok = c.ok & nok[nt];
-      sv[nt] = act_bits_to_float<ACT>(c.s[nt] & ok);   // zero bits -> +0.0f
-      zv[nt] = act_bits_to_float<ACT>(c.z[nt] & ok);
+      const uint32_t sb = c.s[nt] & ok, zb = c.z[nt] & ok;   // zero bits -> +0.0
+      if constexpr (ACT == ACT_F16 && BITS == 4) {
+        sz[nt].s2 = (sb & 0xFFFFu) * 0x10001u;
+        sz[nt].z2 = (zb & 0xFFFFu) * 0x10001u;
+      } else {
+        sz[nt].s = act_bits_to_float<ACT>(sb);
+        sz[nt].z = act_bits_to_float<ACT>(zb);
+      }
     }
   };
 
@@ -326,8 +363,8 @@ __global__ __launch_bounds__(64 * WC * KGR, 1) void qmm_kernel(QmmParams p) {
   // their registers have been issued.  Scheduling barriers pin this order:
   // with one wave per SIMD, the MFMA pipe stays busy only if the VALU work
   // sits between the MFMAs rather than in clusters.
-  auto phase = [&](auto KSc, auto DKSc, const Codes& C, const float (&sv)[NT], const float (&zv)[NT],
-                   const uint4* ns, auto NKSc) {
+  auto phase = [&](auto KSc, auto DKSc, const Codes& C, const ScaleZero (&sz)[NT], const uint4* ns,
+                   auto NKSc) {
     constexpr int KS = decltype(KSc)::value;
     constexpr int DKS = decltype(DKSc)::value;
     constexpr int NKS = decltype(NKSc)::value;
@@ -347,7 +384,7 @@ __global__ __launch_bounds__(64 * WC * KGR, 1) void qmm_kernel(QmmParams p) {
           lo[c] = and_nibbles(C.w[c][DKS]);
           hi[c] = and_nibbles(C.w[c][DKS] >> 4);
         }
-        bw[c][DKS][j] = dq_pair<BITS, ACT, DKS, j>(C.w[c], lo[c], hi[c], sv[c], zv[c]);
+        bw[c][DKS][j] = dq_pair<BITS, ACT, DKS, j>(C.w[c], lo[c], hi[c], sz[c]);
       });
       if constexpr (NKS >= 0 && i == MH * NT - 1)
         read_a(ns, std::integral_constant<int, NKS>{}, I0{}, IMH{});
@@ -380,20 +417,20 @@ __global__ __launch_bounds__(64 * WC * KGR, 1) void qmm_kernel(QmmParams p) {
     load_x((S_) + (X1 ? 1 : 2), XLD);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     {                                                                                         \
-      float sv[NT], zv[NT];                                                                   \
-      scale_zero(CUR, sv, zv);                                                                \
-      phase(K0{}, K3{}, CUR, sv, zv, SR, K1{});                                               \
+      ScaleZero sz[NT];                                                                       \
+      scale_zero(CUR, sz);                                                                    \
+      phase(K0{}, K3{}, CUR, sz, SR, K1{});                                                   \
     }                                                                                         \
     load_codes(wstep((S_) + 2), CUR);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                        \
-    float sv[NT], zv[NT];                                                                     \
-    scale_zero(NXT, sv, zv);                                                                  \
-    phase(K1{}, K0{}, NXT, sv, zv, SR, K2{});                                                 \
+    ScaleZero sz[NT];                                                                         \
+    scale_zero(NXT, sz);                                                                      \
+    phase(K1{}, K0{}, NXT, sz, SR, K2{});                                                     \
     if constexpr (!X1) store_x(XST, SW);                                                      \
-    phase(K2{}, K1{}, NXT, sv, zv, SR, K3{});                                                 \
+    phase(K2{}, K1{}, NXT, sz, SR, K3{});                                                     \
     if constexpr (X1) store_x(XLD, SW);                                                       \
     __syncthreads(); /* stage S_+1 written by every wave; stage S_ fully read */              \
-    phase(K3{}, K2{}, NXT, sv, zv, SW, K0{});                                                 \
+    phase(K3{}, K2{}, NXT, sz, SW, K0{});                                                     \
   }
 
   Codes ca, cb;
@@ -404,13 +441,13 @@ __global__ __launch_bounds__(64 * WC * KGR, 1) void qmm_kernel(QmmParams p) {
   load_codes(wstep(1), cb);
   store_x(xa, stage0);
   {
-    float sv[NT], zv[NT];
-    scale_zero(ca, sv, zv);
+    ScaleZero sz[NT];
+    scale_zero(ca, sz);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint4 b0 = dequant_ksub<BITS, ACT, 0>(ca.w[nt], sv[nt], zv[nt]);
-      const uint4 b1 = dequant_ksub<BITS, ACT, 1>(ca.w[nt], sv[nt], zv[nt]);
-      const uint4 b2 = dequant_ksub<BITS, ACT, 2>(ca.w[nt], sv[nt], zv[nt]);
+      const uint4 b0 = dequant_ksub<BITS, ACT, 0>(ca.w[nt], sz[nt]);
+      const uint4 b1 = dequant_ksub<BITS, ACT, 1>(ca.w[nt], sz[nt]);
+      const uint4 b2 = dequant_ksub<BITS, ACT, 2>(ca.w[nt], sz[nt]);
       bw[nt][0][0] = b0.x; bw[nt][0][1] = b0.y; bw[nt][0][2] = b0.z; bw[nt][0][3] = b0.w;
       bw[nt][1][0] = b1.x; bw[nt][1][1] = b1.y; bw[nt][1][2] = b1.z; bw[nt][1][3] = b1.w;
       bw[nt][2][0] = b2.x; bw[nt][2][1] = b2.y; bw[nt][2][2] = b2.z; bw[nt][2][3] = b2.w;
