@@ -154,16 +154,23 @@ __device__ __forceinline__ uint32_t dq_pair_f16_b4(uint32_t lo, uint32_t hi, con
 
 // Dequantize k-sub KS (codes [8KS, 8KS+8)) of a 32-code run into one MFMA
 // operand: four packed pairs (code 8KS+2j in the low half of dword j).
-// fp16 activations, 1- and 2-bit codes: codes I = 8KS+2J and I+1 sit side by
-// side in one word; one field extract and one shift-or put them in the low
+// fp16 activations, any width: codes I = 8KS+2J and I+1 are 2*BITS adjacent
+// bits of the run (crossing at most one word boundary); a field extract (a
+// funnel shift first where they cross) and one shift-or put them in the low
 // bits of the two halves, then the packed steps of dq_pair_f16_b4.
 template <int BITS, int KS, int J>
-__device__ __forceinline__ uint32_t dq_pair_f16_narrow(const uint32_t (&w)[BITS], const ScaleZero& sz) {
-  static_assert(BITS <= 2, "codes of a pair must share a word");
+__device__ __forceinline__ uint32_t dq_pair_f16_bits(const uint32_t (&w)[BITS], const ScaleZero& sz) {
   constexpr int bit = (8 * KS + 2 * J) * BITS;
+  constexpr int wi = bit / 32, off = bit % 32;
   // the two codes alone (nothing above them, which the shift-or would carry
   // into the high half)
-  const uint32_t x = (w[bit / 32] >> (bit % 32)) & ((1u << (2 * BITS)) - 1u);
+  uint32_t x;
+  if constexpr (off + 2 * BITS <= 32 || off == 0) {
+    x = w[wi] >> off;
+  } else {
+    x = (w[wi] >> off) | (w[wi + 1] << (32 - off));
+  }
+  x &= (1u << (2 * BITS)) - 1u;
   constexpr uint32_t mask = ((1u << BITS) - 1u) * 0x10001u;
   const uint32_t v = ((x | (x << (16 - BITS))) & mask) | 0x64006400u;
   const half2v_t q = __builtin_bit_cast(half2v_t, v) - half2v_t{1024, 1024};
@@ -171,9 +178,9 @@ __device__ __forceinline__ uint32_t dq_pair_f16_narrow(const uint32_t (&w)[BITS]
                                                                 __builtin_bit_cast(half2v_t, sz.z2)));
 }
 
-// Activation types and widths that dequantize in packed fp16 arithmetic.
+// fp16 activations dequantize in packed fp16 arithmetic (every width).
 template <int BITS, int ACT>
-constexpr bool packed_f16_dequant() { return ACT == ACT_F16 && (BITS == 4 || BITS <= 2); }
+constexpr bool packed_f16_dequant() { return ACT == ACT_F16; }
 
 template <int BITS, int ACT, int KS>
 __device__ __forceinline__ uint4 dequant_ksub(const uint32_t (&w)[BITS], const ScaleZero& sz) {
@@ -193,8 +200,8 @@ __device__ __forceinline__ uint4 dequant_ksub(const uint32_t (&w)[BITS], const S
                         pack2<ACT>(__builtin_fmaf(s, ubyte<3>(lo), z), __builtin_fmaf(s, ubyte<3>(hi), z)));
     }
   } else if constexpr (packed_f16_dequant<BITS, ACT>()) {
-    return make_uint4(dq_pair_f16_narrow<BITS, KS, 0>(w, sz), dq_pair_f16_narrow<BITS, KS, 1>(w, sz),
-                      dq_pair_f16_narrow<BITS, KS, 2>(w, sz), dq_pair_f16_narrow<BITS, KS, 3>(w, sz));
+    return make_uint4(dq_pair_f16_bits<BITS, KS, 0>(w, sz), dq_pair_f16_bits<BITS, KS, 1>(w, sz),
+                      dq_pair_f16_bits<BITS, KS, 2>(w, sz), dq_pair_f16_bits<BITS, KS, 3>(w, sz));
   } else {
     return make_uint4(dequant2<BITS, ACT, 8 * KS + 0>(w, sz), dequant2<BITS, ACT, 8 * KS + 2>(w, sz),
                       dequant2<BITS, ACT, 8 * KS + 4>(w, sz), dequant2<BITS, ACT, 8 * KS + 6>(w, sz));
@@ -217,7 +224,7 @@ __device__ __forceinline__ uint32_t dq_pair(const uint32_t (&w)[BITS], uint32_t 
   if constexpr (BITS == 4 && ACT == ACT_F16) {
     return dq_pair_f16_b4<J>(lo, hi, sz);
   } else if constexpr (packed_f16_dequant<BITS, ACT>()) {
-    return dq_pair_f16_narrow<BITS, KS, J>(w, sz);
+    return dq_pair_f16_bits<BITS, KS, J>(w, sz);
   } else if constexpr (BITS == 4) {
     return pack2<ACT>(__builtin_fmaf(sz.s, ubyte<J>(lo), sz.z), __builtin_fmaf(sz.s, ubyte<J>(hi), sz.z));
   } else {
