@@ -125,10 +125,13 @@ const QmvLauncher kQmv[8] = {nullptr,
                              lowbit::launch_qmv_b7};
 
 // Largest M that the automatic choice sends to the decode kernel: measured
-// on MI355X at K = N = 4096, group 64, fp16 -- the decode kernel is faster up
-// to M = 8 for 1-2 bit codes, M = 6 for 3-4 bits and M = 4 for 5-7 bits
-// (it re-reads the weights once per four activation rows).
-inline int64_t qmv_max_m(int bits) { return bits <= 2 ? 8 : bits <= 4 ? 6 : 4; }
+// on MI355X at K = N = 4096, group 64, fp16 and bf16, b = 1..5 and 7 (both
+// paths forced, graph-timed on one box) -- the decode kernel is faster up to
+// M = 4 at every width (e.g. b = 4, fp16, M = 4: 7.7 vs 10.6 us) and the MFMA
+// kernel from M = 5 (b = 4: 10.5 vs 11.2 us; b = 7: 12.7 vs 15.8 us): the
+// decode kernel serves four activation rows per pass and re-reads the
+// weights for the next four.
+inline int64_t qmv_max_m(int /*bits*/) { return 4; }
 static_assert(LOWBIT_MAX_MULTI <= lowbit::kQmvMaxProblems, "one launch serves every desc");
 
 typedef int (*QmvStageBytes)(int);

@@ -74,8 +74,7 @@ typedef enum lowbit_dtype {
 
 /* Which kernel family lowbit_linear_path runs. */
 typedef enum lowbit_path {
-  LOWBIT_PATH_AUTO = 0,  /* qmv for fp32 activations and for M <= 8 (1-2 bit
-                            codes), M <= 6 (3-4 bits), M <= 4 (5-7 bits);
+  LOWBIT_PATH_AUTO = 0,  /* qmv for fp32 activations and for M <= 4;
                             qmm otherwise */
   LOWBIT_PATH_QMV = 1,   /* decode matrix-vector kernel, any M              */
   LOWBIT_PATH_QMM = 2    /* MFMA matrix-matrix kernel, fp16/bf16 only       */
