@@ -419,3 +419,52 @@ def test_workload_sampled(case):
     y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], case.group,
                              None if b is None else bias_values(b)[rows])
     check_close(y[:, torch.from_numpy(rows).to(DEV)], y_ref, A, case.name)
+
+
+def random_shape_cases(chunk: int, count: int = 12):
+    """Seeded random shapes: M from 1 to 160 (both kernels and the crossover),
+    N from 1 to 1500 (ragged row groups and column tiles), K up to 4096 in
+    whole groups (one to many K steps, K splits, one and two rounds per
+    lane), every width, group, activation type and bias choice."""
+    rng = np.random.default_rng(0x5EED + chunk)
+    cases = []
+    for i in range(count):
+        act = ["f32", "f16", "bf16"][int(rng.integers(3))]
+        m_band = int(rng.integers(3))
+        M = int(rng.integers(1, 7)) if m_band == 0 else (int(rng.integers(7, 41)) if m_band == 1
+                                                         else int(rng.integers(41, 161)))
+        if act == "f32":
+            M = min(M, 8)
+        group = [32, 64, 128, 256][int(rng.integers(4))]
+        K = group * int(rng.integers(1, 4096 // group + 1))
+        N = int(rng.integers(1, 1501))
+        bits = int(rng.integers(1, 8))
+        cases.append(Case(f"rnd{chunk}_{i}", M, K, N, bits, group, act,
+                          bias=bool(rng.integers(2)), seed=1000 * chunk + i))
+    return cases
+
+
+@pytest.mark.parametrize("chunk", range(12))
+def test_random_shapes(chunk):
+    """GPU quantizer bit-exact and the linear within tolerance of the oracle,
+    on the default path and on every forced path the activation type allows,
+    for seeded random shapes."""
+    for case in random_shape_cases(chunk):
+        what = (f"{case.name}: M={case.M} N={case.N} K={case.K} b={case.bits} "
+                f"g={case.group} {case.act} bias={case.bias}")
+        W = weight_for(case)
+        ref = oracle.quantize(W.numpy(), case.bits, case.group, case.act)
+        packed, s, z, codes = gpu_quantize(W, case.bits, case.group, case.act)
+        torch.cuda.synchronize()
+        assert_quant_equal(ref, packed, s, z, codes, case.bits)
+        x = make_x(case)
+        b = make_bias(case)
+        y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], case.group,
+                                 bias_values(b))
+        xd = x.to(DEV)
+        bd = None if b is None else b.to(DEV)
+        paths = [lb.PATH_AUTO, lb.PATH_QMV] + ([lb.PATH_QMM] if case.act != "f32" else [])
+        for path in paths:
+            y = lb.lowbit_linear(xd, packed, s, z, bd, case.bits, case.group, path=path)
+            torch.cuda.synchronize()
+            check_close(y, y_ref, A, f"{what} path={path}")
