@@ -62,3 +62,39 @@ def test_multi_llama_layer_shapes():
         outs = lb.lowbit_linear_multi(items, bits, group)
         for (xx, packed, s, z, _, _), y in zip(items, outs):
             assert torch.equal(y, lb.lowbit_linear(xx, packed, s, z, None, bits, group, path=lb.PATH_QMV))
+
+
+@pytest.mark.parametrize("chunk", range(12))
+def test_multi_random_mixes(chunk):
+    """Seeded random mixes of 1-8 problems in one launch: every N from 1 to
+    1200, K from one group to 12288 (one to three rounds per lane, lane
+    groups of different widths side by side), M from 1 to 6, with and
+    without bias; each output equals its separate decode-path call bit for
+    bit and matches the oracle."""
+    rng = np.random.default_rng(0xA11 + chunk)
+    bits = int(rng.integers(1, 8))
+    group = [32, 64, 128, 256][int(rng.integers(4))]
+    act = ["f32", "f16", "bf16"][int(rng.integers(3))]
+    M = int(rng.integers(1, 7))
+    count = int(rng.integers(1, lb.MAX_MULTI + 1))
+    items, refs = [], []
+    for i in range(count):
+        N = int(rng.integers(1, 1201))
+        K = group * int(rng.integers(1, 12288 // group + 1))
+        ref, (packed, s, z) = quantized(N, K, bits, group, act, seed=100 * chunk + i)
+        x = make_x(Case("x", M, K, 1, bits, group, act, seed=1000 * chunk + i))
+        b = None
+        if rng.integers(2):
+            b = (torch.randn(N, generator=torch.Generator().manual_seed(i)) * 0.1).to(TORCH_ACT[act])
+        items.append((x.to(DEV), packed, s, z, None if b is None else b.to(DEV), None))
+        refs.append((ref, x, b, N, K))
+    outs = lb.lowbit_linear_multi(items, bits, group)
+    torch.cuda.synchronize()
+    for (xd, packed, s, z, bd, _), y, (ref, x, b, N, K) in zip(items, outs, refs):
+        what = f"multi chunk={chunk} b={bits} g={group} {act} M={M} N={N} K={K}"
+        single = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, path=lb.PATH_QMV)
+        torch.cuda.synchronize()
+        assert torch.equal(y, single), what
+        y_ref, A = oracle.linear(x.float().numpy(), ref["q"], ref["s"], ref["z"], group,
+                                 None if b is None else b.float().numpy())
+        check_close(y, y_ref, A, what)
