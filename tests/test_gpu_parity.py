@@ -60,9 +60,10 @@ def test_quantize_small(bits, group, act):
 
 @pytest.mark.parametrize("act", ["f32", "f16", "bf16"])
 def test_quantize_edge_values(act):
-    """Constant groups, signed zeros, exact grids and ties inside real rows."""
+    """Constant groups, signed zeros, exact grids, ties, subnormal weights and
+    scales, and the order-of-rounding cases, inside real rows."""
     rng = np.random.default_rng(11)
-    bits, group, K, N = 4, 32, 256, 9
+    bits, group, K, N = 4, 32, 256, 11
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     W[0, :32] = 0.0
     W[0, 32:64] = -0.0
@@ -72,6 +73,18 @@ def test_quantize_edge_values(act):
     W[3, 32:64] = (-(2.0 ** -3) + 2.0 ** -8 * ((np.arange(32) % 15) + 0.5)).astype(np.float32)
     W[3, 32], W[3, 33] = -(2.0 ** -3), -(2.0 ** -3) + 15 * 2.0 ** -8
     W[4, :] = 1e-30
+    # fp32-subnormal weights (below 2^-126), alone and mixed with normal ones
+    W[5, :32] = (np.arange(32) * 3e-42).astype(np.float32)
+    W[5, 32:64] = (rng.standard_normal(32) * 1e-38).astype(np.float32)
+    # scales that are fp16 subnormals (below 2^-14): max - min = 0.7 * 2^-14
+    W[6, :32] = (np.linspace(0.0, 0.7 * 2.0 ** -14, 32) + 0.25).astype(np.float32)
+    W[6, 32:64] = (rng.random(32) * 2.0 ** -17).astype(np.float32)
+    W[6, 32] = 0.0
+    # the hand-derived order-of-rounding groups of the oracle's R6 pins
+    from tests.test_oracle_quantize import R6_CASES
+    for i, case in enumerate(R6_CASES):
+        Wc, _, _, _ = case("f16" if act == "f32" else act)
+        W[7 + i, :32] = Wc[0]
     Wt = torch.from_numpy(W)
     ref = oracle.quantize(W, bits, group, act)
     packed, s, z, codes = gpu_quantize(Wt, bits, group, act)

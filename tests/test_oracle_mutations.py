@@ -108,3 +108,25 @@ def test_quantizer_mutants_fail_pins():
 def test_bigint_formulation_is_not_the_oracle():
     # sanity: the independent formulation really is independent of numpy packbits
     assert bigint_pack_row([1, 2, 3, 4, 5, 6, 7, 0], 3).hex() == "d1581f"
+
+
+def quantize_codes_from_unrounded(W, bits, group, dtype):
+    """Mutant of R6: codes from the fp32 scale and zero before they are rounded
+    to the storage dtype (the stored s and z are still returned rounded)."""
+    out = oracle.quantize(W, bits, group, dtype)
+    N, K = W.shape
+    s = np.repeat(out["s32"], group, axis=1).astype(np.float32)
+    z = np.repeat(out["z32"], group, axis=1).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = ((W - z) / np.where(s == 0, np.float32(1), s)).astype(np.float32)
+    q = np.clip(np.rint(t), 0, (1 << bits) - 1)
+    out["q"] = np.where(s != 0, q, 0).astype(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_r6_mutant_fails_pins(dtype):
+    from tests.test_oracle_quantize import R6_CASES
+    for case in R6_CASES:
+        W, _, _, codes = case(dtype)
+        assert list(quantize_codes_from_unrounded(W, 4, 32, dtype)["q"][0]) != codes

@@ -183,3 +183,57 @@ def test_rejects_nonfinite_and_range():
         oracle.quantize(np.zeros((1, 48), np.float32), 4, 32, "f16")
     with pytest.raises(ValueError):
         oracle.quantize(np.zeros((1, 64), np.float32), 8, 32, "f16")
+
+
+# ------------------------------------------------- R6: order of rounding --
+# Codes are computed from the STORED (rounded) scale and zero, not from the
+# fp32 values before rounding.  Each case below is derived by hand so that the
+# two rules give different codes; the page "metal lowbit kernels: qmv_fast
+# optimization" (Summary) has the kernels consume scales and zeros exactly as
+# the quantize function stores them, so the codes must be a function of those
+# stored values.
+
+def _r6_scale_case(dtype):
+    """Group of 32 at 4 bits: min 0, max 1, and one weight w.
+
+    s32 = fp32(1/15).  Stored: fp16 1/15 -> 1092 * 2^-14 = 0.066650390625
+    (bits 0x2C44, below 1/15); bf16 1/15 -> 137 * 2^-11 = 0.06689453125 (bits
+    0x3D89, above 1/15).  z = 0 is exact in every dtype.
+      fp16, w = 0.9665: w / s_st = 14.501 -> 15, while 15 * w = 14.4975 -> 14.
+      bf16, w = 0.968:  w / s_st = 14.471 -> 14, while 15 * w = 14.52 -> 15.
+    """
+    w, s_bits, code_w = {"f16": (0.9665, 0x2C44, 15), "bf16": (0.968, 0x3D89, 14)}[dtype]
+    W = np.zeros((1, 32), np.float32)
+    W[0, 1], W[0, 2] = 1.0, w
+    return W, s_bits, 0x0000, [0, 15, code_w] + [0] * 29
+
+
+def _r6_zero_case(dtype):
+    """Group of 32 at 4 bits: min = fp32(-0.1) (bits 0xBDCCCCCD), max = min +
+    15 * 2^-6 (fp32 bits 0x3E09999A), so s = 2^-6 exactly in every dtype.
+    Stored zero: fp16 -0.1 -> -0.0999755859375 (0xAE66, 2.44e-5 above);
+    bf16 -0.1 -> -0.10009765625 (0xBDCD, 9.77e-5 below).
+      fp16, w bits 0x3C8CED90: (w - z32) / s = 7.5010 -> 8, (w - z_st) / s = 7.4994 -> 7.
+      bf16, w bits 0x3C8C6A80: (w - z32) / s = 7.4970 -> 7, (w - z_st) / s = 7.5033 -> 8.
+    """
+    wbits, z_bits, s_bits, code_w = {"f16": (0x3C8CED90, 0xAE66, 0x2400, 7),
+                                      "bf16": (0x3C8C6A80, 0xBDCD, 0x3C80, 8)}[dtype]
+    W = np.zeros((1, 32), np.float32)
+    W[0, 0] = np.float32(-0.1)
+    W[0, 1] = np.array([0x3E09999A], np.uint32).view(np.float32)[0]
+    W[0, 2] = np.array([wbits], np.uint32).view(np.float32)[0]
+    W[0, 3:] = W[0, 0]
+    return W, s_bits, z_bits, [0, 15, code_w] + [0] * 29
+
+
+R6_CASES = [_r6_scale_case, _r6_zero_case]
+
+
+@pytest.mark.parametrize("case", R6_CASES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_r6_codes_from_stored_scale_and_zero(case, dtype):
+    W, s_bits, z_bits, codes = case(dtype)
+    out = oracle.quantize(W, 4, 32, dtype)
+    assert int(out["s_bits"][0, 0]) == s_bits
+    assert int(out["z_bits"][0, 0]) == z_bits
+    assert list(out["q"][0]) == codes
