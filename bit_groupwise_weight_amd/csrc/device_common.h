@@ -89,20 +89,10 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
   }
 }
 
-// OR-ing a code q (< 2^7) into the mantissa of this 16-bit constant gives the
-// value MAGIC + q exactly: fp16 1024.0 (ulp 1 on [1024, 2048)), bf16 128.0
-// (ulp 1 on [128, 256)).
+// Two ones of the activation type in one word: dot2 with it sums a pair.
 template <int ACT> struct Magic;
-template <> struct Magic<ACT_F16> {
-  static constexpr uint32_t pair = 0x64006400u;
-  static constexpr uint32_t ones = 0x3c003c00u;
-  static constexpr float value = 1024.0f;
-};
-template <> struct Magic<ACT_BF16> {
-  static constexpr uint32_t pair = 0x43004300u;
-  static constexpr uint32_t ones = 0x3f803f80u;
-  static constexpr float value = 128.0f;
-};
+template <> struct Magic<ACT_F16> { static constexpr uint32_t ones = 0x3c003c00u; };
+template <> struct Magic<ACT_BF16> { static constexpr uint32_t ones = 0x3f803f80u; };
 
 // ---- cross-lane sums with DPP ----------------------------------------------
 // x + (x moved by a DPP pattern); lanes outside row_mask add 0.

@@ -12,14 +12,18 @@
 //     span of the packed row;
 //   * the block stages the activations of the round once in LDS, already
 //     rearranged into the operand pairs the unpack plan needs, together with
-//     each 32-code run's activation sum X and constant part C; activation
+//     each 32-code run's activation sum X; activation
 //     loads are issued before the weight loads so the stage is ready while the
 //     weights are still in flight;
-//   * fp16: codes become fp16 values by OR-ing exponent fields (see
-//     qmv_plan.h) and are multiplied in pairs by v_dot2_f32_f16; bf16 uses the
-//     same trick with the fixed constant 128; fp32 converts each code;
+//   * codes reach the dot products as exact values: fp16 codes by OR-ing
+//     exponent fields (see qmv_plan.h), which gives 2^(10-o) + q, and one
+//     packed fp16 subtract of 2^(10-o) per pair, then v_dot2_f32_f16; bf16
+//     codes through the fp8 conversion (a code below 16 in a byte is the
+//     e4m3 value q * 2^-9) or, above 4 bits, through fp32; fp32 converts
+//     each code.  Only the products x*q enter the fp32 sums, so their
+//     rounding is relative to sum |x*q| and not to a large constant part;
 //   * per 32-code run (which never crosses a group):
-//       y += s * (sum_k x_k q_k) + z * X,  sum_k x_k q_k = P - C;
+//       y += s * (sum_k x_k q_k) + z * X;
 //   * the R row partial sums of the lanes of a row group are combined with
 //     DPP lane moves; bias is added in fp32 and the result rounded once.
 #include "device_common.h"
@@ -38,33 +42,30 @@ template <int ACT, int BITS> struct StagedWords;
 template <int BITS> struct StagedWords<ACT_F16, BITS> { static constexpr int n = F16Plan<BITS>::n; };
 template <int BITS> struct StagedWords<ACT_BF16, BITS> { static constexpr int n = 16; };
 template <int BITS> struct StagedWords<ACT_F32, BITS> { static constexpr int n = 32; };
-// uint4 quads per staged run: the words, then X and C, padded to 16 bytes.
+// uint4 quads per staged run: the words, then X, padded to 16 bytes.
 template <int ACT, int BITS> struct RunQuads {
-  static constexpr int n = (StagedWords<ACT, BITS>::n + 2 + 3) / 4;
+  static constexpr int n = (StagedWords<ACT, BITS>::n + 1 + 3) / 4;
 };
 
 // ---------------------------------------------------------------- staging --
 
-template <int ACT, int BITS, int I = 0>
-__device__ __forceinline__ void f16_stage_slots(const uint32_t* raw, uint32_t* out, float& C) {
+template <int BITS, int I = 0>
+__device__ __forceinline__ void f16_stage_slots(const uint32_t* raw, uint32_t* out) {
   if constexpr (I < F16Plan<BITS>::n) {
     constexpr PairSlot s = F16Plan<BITS>::table.s[I];
     uint32_t lo = 0, hi = 0;
     if constexpr (s.klo >= 0) lo = (raw[s.klo >> 1] >> ((s.klo & 1) * 16)) & 0xffffu;
     if constexpr (s.khi >= 0) hi = (raw[s.khi >> 1] >> ((s.khi & 1) * 16)) & 0xffffu;
-    const uint32_t w = lo | (hi << 16);
-    out[I] = w;
-    constexpr uint32_t mag = f16_magic_for_offset(s.olo) | (f16_magic_for_offset(s.ohi) << 16);
-    C = dot2<ACT_F16>(w, mag, C);
-    f16_stage_slots<ACT, BITS, I + 1>(raw, out, C);
+    out[I] = lo | (hi << 16);
+    f16_stage_slots<BITS, I + 1>(raw, out);
   }
 }
 
-// Turn 32 raw activations into the staged words of one run (+ X, C).
+// Turn 32 raw activations into the staged words of one run (+ X).
 template <int ACT, int BITS>
 __device__ __forceinline__ void stage_run(const uint32_t* raw, uint32_t* out) {
   constexpr int W = StagedWords<ACT, BITS>::n;
-  float X = 0.0f, C = 0.0f;
+  float X = 0.0f;
   if constexpr (ACT == ACT_F32) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) { out[i] = raw[i]; X += __uint_as_float(raw[i]); }
@@ -72,17 +73,15 @@ __device__ __forceinline__ void stage_run(const uint32_t* raw, uint32_t* out) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) X = dot2<ACT>(raw[i], Magic<ACT>::ones, X);
     if constexpr (ACT == ACT_F16) {
-      f16_stage_slots<ACT, BITS>(raw, out, C);
+      f16_stage_slots<BITS>(raw, out);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) out[i] = raw[i];
-      C = Magic<ACT>::value * X;
     }
   }
   out[W] = __float_as_uint(X);
-  out[W + 1] = __float_as_uint(C);
 #pragma unroll
-  for (int i = W + 2; i < RunQuads<ACT, BITS>::n * 4; ++i) out[i] = 0u;
+  for (int i = W + 1; i < RunQuads<ACT, BITS>::n * 4; ++i) out[i] = 0u;
 }
 
 // ------------------------------------------------------------------ dots --
@@ -110,20 +109,41 @@ __device__ __forceinline__ float f16_dot_slots(const uint32_t* w, const uint32_t
                               (s.khi >= 0 ? (m << (16 + s.ohi)) : 0u);
     constexpr uint32_t mag = f16_magic_for_offset(s.olo) | (f16_magic_for_offset(s.ohi) << 16);
     // mag lives in a VGPR so that the AND and the OR fuse into one
-    // v_and_or_b32 (a VOP3 form may read one scalar constant: the mask)
-    acc = dot2<ACT_F16>(xs[I], (win & mask) | in_vgpr(mag), acc);
+    // v_and_or_b32 (a VOP3 form may read one scalar constant: the mask).
+    // Each half then reads 2^(10-o) + q exactly; subtracting 2^(10-o) is
+    // exact too (q < 2^(10-o)), which leaves the codes themselves.
+    const uint32_t v = (win & mask) | in_vgpr(mag);
+    constexpr _Float16 mlo = static_cast<_Float16>(1u << (10 - s.olo));
+    constexpr _Float16 mhi = static_cast<_Float16>(1u << (10 - s.ohi));
+    const half2_t q = __builtin_bit_cast(half2_t, v) - half2_t{mlo, mhi};
+    acc = dot2<ACT_F16>(xs[I], __builtin_bit_cast(uint32_t, q), acc);
     return f16_dot_slots<BITS, I + 1>(w, xs, acc);
   } else {
     return acc;
   }
 }
 
+// Codes 2I and 2I+1 of a run as two exact bf16 values (low half: code 2I).
+// Up to 4 bits, a code q in a byte is the OCP fp8 e4m3 value q * 2^-9 (a
+// subnormal below 8, then the first binade with step 2^-9), so one scaled
+// fp8 conversion by 2^9 gives both; wider codes go through fp32, where the
+// bf16 value is the top half of the fp32 one (exact for q < 256).
+template <int BITS, int I>
+__device__ __forceinline__ uint32_t bf16_code_pair(const uint32_t* w) {
+  if constexpr (BITS <= 4) {
+    const uint32_t b = code_at<BITS, 2 * I>(w) | (code_at<BITS, 2 * I + 1>(w) << 8);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 512.0f, false));
+  } else {
+    const uint32_t f0 = __float_as_uint(static_cast<float>(code_at<BITS, 2 * I>(w)));
+    const uint32_t f1 = __float_as_uint(static_cast<float>(code_at<BITS, 2 * I + 1>(w)));
+    return __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+  }
+}
+
 template <int BITS, int I = 0>
 __device__ __forceinline__ float bf16_dot_pairs(const uint32_t* w, const uint32_t* xs, float acc) {
   if constexpr (I < 16) {
-    const uint32_t h = code_at<BITS, 2 * I>(w) | (code_at<BITS, 2 * I + 1>(w) << 16) |
-                       Magic<ACT_BF16>::pair;
-    acc = dot2<ACT_BF16>(xs[I], h, acc);
+    acc = dot2<ACT_BF16>(xs[I], bf16_code_pair<BITS, I>(w), acc);
     return bf16_dot_pairs<BITS, I + 1>(w, xs, acc);
   } else {
     return acc;
@@ -143,11 +163,10 @@ __device__ __forceinline__ float f32_dot(const uint32_t* w, const uint32_t* xs, 
 // sum_k x_k q_k over one run, from the staged words and the run's code words.
 template <int ACT, int BITS>
 __device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) {
-  constexpr int W = StagedWords<ACT, BITS>::n;
   if constexpr (ACT == ACT_F16) {
-    return f16_dot_slots<BITS>(w, xs, 0.0f) - __uint_as_float(xs[W + 1]);
+    return f16_dot_slots<BITS>(w, xs, 0.0f);
   } else if constexpr (ACT == ACT_BF16) {
-    return bf16_dot_pairs<BITS>(w, xs, 0.0f) - __uint_as_float(xs[W + 1]);
+    return bf16_dot_pairs<BITS>(w, xs, 0.0f);
   } else {
     return f32_dot<BITS>(w, xs, 0.0f);
   }

@@ -20,3 +20,20 @@ def lowbit_lib():
         import __graft_entry__
         __graft_entry__.build()
     return lowbit.load()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst err/tol of the output comparisons of the GPU tests (when any ran):
+    the headroom against 1e-3 + 2e-3 * sum |x*w| per case family."""
+    helpers = sys.modules.get("tests.gpu_helpers")
+    log = getattr(helpers, "ERR_TOL_LOG", None)
+    if not log:
+        return
+    fam = {}
+    for what, r in log:
+        key = what.split(":")[0].split(" M=")[0]
+        if r >= fam.get(key, (-1.0, ""))[0]:
+            fam[key] = (r, what)
+    terminalreporter.write_sep("-", f"worst err/tol over {len(log)} output comparisons")
+    for key, (r, what) in sorted(fam.items(), key=lambda kv: -kv[1][0])[:40]:
+        terminalreporter.write_line(f"{r:8.4f}  {what}")

@@ -39,14 +39,21 @@ def upload_quant(q, s, z, bits, act):
     return packed, s_t, z_t
 
 
+# (label, worst err/tol) of every comparison in this session, printed by the
+# terminal summary of tests/conftest.py
+ERR_TOL_LOG = []
+
+
 def check_close(y_gpu: torch.Tensor, y_ref: np.ndarray, A: np.ndarray, what: str):
     y = y_gpu.detach().float().cpu().numpy().astype(np.float64)
     err = np.abs(y - y_ref)
     tol = oracle.tolerance(A)
     bad = err > tol
+    ratio = float((err / tol).max()) if err.size else 0.0
+    ERR_TOL_LOG.append((what, ratio))
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance; worst "
                            f"err {err.max():.3e} (tol there {tol.flat[int(err.argmax())]:.3e})")
-    return float((err / tol).max())
+    return ratio
 
 
 def x_values(x: torch.Tensor) -> np.ndarray:
