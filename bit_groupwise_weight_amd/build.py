@@ -41,7 +41,8 @@ def hipcc() -> str:
 def _units():
     units = [("lowbit_api.cpp", "lowbit_api.o", []),
              ("quant_pack.hip", "quant_pack.o", ["-ffp-contract=off"]),
-             ("probe.hip", "probe.o", [])]
+             ("probe.hip", "probe.o", []),
+             ("device_scratch.hip", "device_scratch.o", [])]
     for b in range(1, 8):
         units.append(("qmv.hip", f"qmv_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
         units.append(("qmm.hip", f"qmm_b{b}.o", [f"-DLOWBIT_BITS={b}"]))

@@ -128,6 +128,16 @@ hipError_t launch_qmm_b5(const QmmParams&, const QmmLaunch&, int act, hipStream_
 hipError_t launch_qmm_b6(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b7(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 
+// ------------------------------------------------- library-owned scratch --
+// Size of the device array behind lowbit_linear_noalloc (per device).  The
+// largest K-split schedule of the MFMA path writes one fp32 partial per
+// output of a block tile per block, at most (CUs) x (128 x 256) x 4 bytes =
+// 32 MiB on a 256-CU device.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+// Device address of this device's copy of the array (looked up once per
+// device, with that device current).
+hipError_t noalloc_scratch(void** out);
+
 // ------------------------------------------------------- measurement probes --
 // Plain streaming read of `bytes` (multiple of 16) with loads_per_thread
 // (1, 2, 4 or 8) 16-byte loads per thread and round.

@@ -560,6 +560,36 @@ lowbit_status lowbit_linear(const void* x, lowbit_dtype act_dtype, const uint8_t
                             workspace, workspace_bytes, LOWBIT_PATH_AUTO, stream);
 }
 
+lowbit_status lowbit_linear_noalloc(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                                    const void* scales, const void* zeros, const void* bias, void* y,
+                                    int bits, int group, int64_t M, int64_t N, int64_t K,
+                                    void* stream) {
+  g_last_error.clear();
+  lowbit_status st = check_linear(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K);
+  if (st != LOWBIT_OK) return st;
+  if (M == 0) return LOWBIT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool use_qmm = (M > qmv_max_m(bits)) && act_dtype != LOWBIT_F32;
+  if (!use_qmm) return run_qmv(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
+  // the schedule lowbit_linear takes with a full workspace, its partial
+  // planes in the library's device array
+  const QmmSchedule sc = qmm_schedule(bits, M, N, K);
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (sc.partial_bytes > 0) {
+    if (sc.partial_bytes > lowbit::kNoallocScratchBytes)
+      return fail(LOWBIT_ERR_WORKSPACE,
+                  "this problem's K split needs %zu bytes of scratch, more than the %zu bytes of the "
+                  "library's device array; call lowbit_linear with a workspace",
+                  sc.partial_bytes, lowbit::kNoallocScratchBytes);
+    const hipError_t e = lowbit::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    scratch_bytes = lowbit::kNoallocScratchBytes;
+  }
+  return run_qmm(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, scratch,
+                 scratch_bytes, s);
+}
+
 lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lowbit_dtype act_dtype,
                                   int bits, int group, int64_t M, void* stream) {
   g_last_error.clear();

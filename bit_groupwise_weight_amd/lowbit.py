@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "lowbit_abi_version", "lowbit_packed_bytes", "lowbit_num_groups", "lowbit_quantize_pack",
     "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path", "lowbit_linear_multi",
     "lowbit_status_string", "lowbit_last_error", "lowbit_probe_stream_read", "lowbit_probe_chase",
+    "lowbit_linear_noalloc",
 )
 MAX_MULTI = 8   # LOWBIT_MAX_MULTI
 
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.lowbit_linear.argtypes = lin + [vp]
     lib.lowbit_linear_path.restype = ctypes.c_int
     lib.lowbit_linear_path.argtypes = lin + [ctypes.c_int, vp]
+    lib.lowbit_linear_noalloc.restype = ctypes.c_int
+    lib.lowbit_linear_noalloc.argtypes = lin[:12] + [vp]
     lib.lowbit_linear_multi.restype = ctypes.c_int
     lib.lowbit_linear_multi.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, c_i64, vp]
@@ -293,6 +296,24 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
         else:
             st = lib.lowbit_linear_path(*args, int(path), s)
     _check(st, "lowbit_linear" if path is None else "lowbit_linear_path")
+    return y
+
+
+def lowbit_linear_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                          zeros: torch.Tensor, bias: Optional[torch.Tensor], bits: int, group: int,
+                          y: torch.Tensor, stream=None) -> torch.Tensor:
+    """lowbit_linear that allocates nothing: `y` is required, and the split-K
+    partials of the MFMA schedule live in the library's own device array
+    (calls that overlap in time on one GPU race; calls on one stream are safe)."""
+    lib = load()
+    _expect(y is not None, "y is required (this call allocates nothing)")
+    M, N, K = _check_linear_tensors(x, packed, scales, zeros, bias, y, bits, group)
+    _require_cuda(x, packed, scales, zeros, bias, y)
+    with torch.cuda.device(x.device):
+        st = lib.lowbit_linear_noalloc(_ptr(x), _DTYPE_ENUM[x.dtype], _ptr(packed), _ptr(scales),
+                                       _ptr(zeros), _ptr(bias), _ptr(y), bits, group, M, N, K,
+                                       _stream_handle(x.device, stream))
+    _check(st, "lowbit_linear_noalloc")
     return y
 
 

@@ -155,6 +155,27 @@ lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const ui
                                  void* workspace, size_t workspace_bytes, lowbit_path path,
                                  void* stream);
 
+/* lowbit_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and results as lowbit_linear without the workspace: the split-K
+ * partial planes of the MFMA schedule live in a device array that the
+ * library holds on every GPU it runs on (LOWBIT_NOALLOC_SCRATCH_BYTES =
+ * 32 MiB, kept until the process ends).  The call allocates nothing (no
+ * hipMalloc, no allocating library routine) and takes the schedule
+ * lowbit_linear takes with a workspace of lowbit_linear_workspace_bytes(),
+ * so its output is bitwise identical to that call's.  A problem whose
+ * schedule needs more than the array holds returns LOWBIT_ERR_WORKSPACE and
+ * launches nothing (on a 256-CU device every shape fits).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results; calls on one
+ * stream run in order and are safe.  The array needs no clearing: each call
+ * writes every partial it reads. */
+#define LOWBIT_NOALLOC_SCRATCH_BYTES (32u << 20)
+lowbit_status lowbit_linear_noalloc(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
+                                    const void* scales, const void* zeros, const void* bias, void* y,
+                                    int bits, int group, int64_t M, int64_t N, int64_t K,
+                                    void* stream);
+
 /* One linear of a lowbit_linear_multi call (pointers as in lowbit_linear). */
 typedef struct lowbit_linear_desc {
   const void* x;          /* device, M x K row-major, act_dtype */
