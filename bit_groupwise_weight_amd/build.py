@@ -46,6 +46,8 @@ def _units():
     for b in range(1, 8):
         units.append(("qmv.hip", f"qmv_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
         units.append(("qmm.hip", f"qmm_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
+        units.append(("qmm_bf16.hip", f"qmm_bf16_b{b}.o",
+                      [f"-DLOWBIT_BITS={b}", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]))
     return units
 
 

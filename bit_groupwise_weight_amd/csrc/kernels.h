@@ -127,6 +127,15 @@ hipError_t launch_qmm_b4(const QmmParams&, const QmmLaunch&, int act, hipStream_
 hipError_t launch_qmm_b5(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b6(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b7(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+// The bf16 kernel's main launch (code operands; 4 column waves, nt == 2,
+// one K group); launch_qmm_b<bits> calls it and adds the split-K reduce.
+hipError_t launch_qmm_bf16_b1(const QmmParams&, const QmmLaunch&, hipStream_t);
+hipError_t launch_qmm_bf16_b2(const QmmParams&, const QmmLaunch&, hipStream_t);
+hipError_t launch_qmm_bf16_b3(const QmmParams&, const QmmLaunch&, hipStream_t);
+hipError_t launch_qmm_bf16_b4(const QmmParams&, const QmmLaunch&, hipStream_t);
+hipError_t launch_qmm_bf16_b5(const QmmParams&, const QmmLaunch&, hipStream_t);
+hipError_t launch_qmm_bf16_b6(const QmmParams&, const QmmLaunch&, hipStream_t);
+hipError_t launch_qmm_bf16_b7(const QmmParams&, const QmmLaunch&, hipStream_t);
 
 // ------------------------------------------------- library-owned scratch --
 // Size of the device array behind lowbit_linear_noalloc (per device).  The

@@ -336,12 +336,19 @@ constexpr int kQmmNarrowMaxSteps = 16;
 // (M = 64, K = N = 4096: 17.25 vs 16.8).
 constexpr int kQmmKGroupsMinSteps = 8;
 
-QmmSchedule qmm_schedule(int bits, int64_t M, int64_t N, int64_t K) {
+QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   const int mtt_env = env_int("LOWBIT_QMM_MTT", 0);
   if (mtt_env == 1 || mtt_env == 2 || mtt_env == 4 || mtt_env == 8) sc.mtt = std::min(sc.mtt, mtt_env);
   sc.nt = 2;
+  if (act == LOWBIT_BF16) {
+    // bf16: the code-operand kernel, 4 column waves of two column tiles
+    sc.waves = 4;
+    sc.kgroups = 1;
+    qmm_split(sc, M, N, K);
+    return sc;
+  }
   // Two K groups of 4 column waves (8 waves, 128 columns) keep two waves per
   // SIMD at the tile width of a 4-wave block, so the K split across blocks
   // stays that of the 4-wave block: one wave's dequantization runs under the
@@ -383,7 +390,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
                       const void* zeros, const void* bias, void* y, int bits, int group,
                       int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
-  QmmSchedule sc = qmm_schedule(bits, M, N, K);
+  QmmSchedule sc = qmm_schedule(bits, act, M, N, K);
   if (sc.splits > 1 && (workspace == nullptr || workspace_bytes < sc.partial_bytes)) {
     sc.splits = 1;                               // no workspace: one block per tile over all K
     sc.ksteps_per_split = static_cast<int>(sc.ksteps);
@@ -518,7 +525,7 @@ size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, 
       M > kMaxDim || N > kMaxDim || K > kMaxDim || !valid_dtype(act_dtype))
     return 0;
   if (act_dtype == LOWBIT_F32) return 0;         // fp32 runs the decode kernel only
-  const QmmSchedule sc = qmm_schedule(bits, M, N, K);
+  const QmmSchedule sc = qmm_schedule(bits, act_dtype, M, N, K);
   return sc.partial_bytes;
 }
 
@@ -573,7 +580,7 @@ lowbit_status lowbit_linear_noalloc(const void* x, lowbit_dtype act_dtype, const
   if (!use_qmm) return run_qmv(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
   // the schedule lowbit_linear takes with a full workspace, its partial
   // planes in the library's device array
-  const QmmSchedule sc = qmm_schedule(bits, M, N, K);
+  const QmmSchedule sc = qmm_schedule(bits, act_dtype, M, N, K);
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
   if (sc.partial_bytes > 0) {

@@ -154,12 +154,13 @@ def test_probe_chase_validation(lowbit_lib, args, status):
 
 
 @pytest.mark.parametrize("M,K,N,bits,group,dtype,planes", [
-    (128, 4096, 14336, 4, 128, "bf16", 2),    # two K groups, 112 tiles, split in 2
-    (128, 14336, 4096, 4, 128, "bf16", 8),    # two K groups, 32 tiles, split in 8
-    (128, 1024, 14336, 4, 128, "bf16", 0),    # short loop: 64-column tiles, no split
+    (128, 4096, 14336, 4, 128, "bf16", 2),    # bf16 kernel: 112 tiles, split in 2
+    (128, 14336, 4096, 4, 128, "bf16", 8),    # bf16 kernel: 32 tiles, split in 8
+    (128, 1024, 14336, 4, 128, "bf16", 2),    # bf16 kernel: 128-column tiles at any K
+    (128, 1024, 14336, 4, 128, "f16", 0),     # fp16, short loop: 64-column tiles, no split
     (64, 4096, 4096, 4, 64, "f16", 8),        # 4 steps per block: one K group
     (64, 4096, 14336, 4, 64, "f16", 2),       # 16 steps per block: two K groups
-    (128, 4096, 14336, 7, 128, "bf16", 2),    # 7 bits: 4-wave blocks
+    (128, 4096, 14336, 7, 128, "f16", 2),     # 7 bits: 4-wave blocks
     (16, 4096, 4096, 4, 64, "f16", 8),
 ])
 def test_mfma_schedule_workspace(lowbit_lib, M, K, N, bits, group, dtype, planes):

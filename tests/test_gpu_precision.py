@@ -138,6 +138,4 @@ def test_correlated_weight_rounding(M, act):
     z = np.where(np.arange(G) % 2 == 0, 1.0, -1.0078125).astype(np.float32)[None, :].repeat(N, 0)
     q = np.ones((N, K), np.uint8)
     x = np.ones((M, K), np.float32)
-    # the bf16 MFMA kernel still rounds s*q + z to bf16 before the MFMA
-    skip = ("qmm",) if act == "bf16" else ()
-    run_paths(x, q, s, z, None, bits, group, act, f"correlated-rounding M={M} {act}", skip=skip)
+    run_paths(x, q, s, z, None, bits, group, act, f"correlated-rounding M={M} {act}")
