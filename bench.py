@@ -115,6 +115,7 @@ def algo_bytes(case) -> int:
 def prepare(case, copies, dev):
     """Quantize once on the GPU and make `copies` independent copies of the weights."""
     from bit_groupwise_weight_amd import lowbit as lb
+from bit_groupwise_weight_amd import probe
     from bit_groupwise_weight_amd.workloads import make_bias, make_weight, make_x
     act = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.act]
     W = make_weight(case).to(dev)
@@ -248,7 +249,7 @@ def single_launch_floor(byte_counts, qmv_us, dev, stream, reps):
         best, best_lpt = None, None
         for lpt in (1, 2, 4, 8):
             def fn(i, s, lpt=lpt):
-                lb.lowbit_probe_stream_read(buf[(i % n) * slot:], nb16, lpt, sink, stream=s)
+                probe.stream_read(buf[(i % n) * slot:], nb16, lpt, sink, stream=s)
             for i in range(3):
                 fn(i, stream)
             g = capture(fn, n, stream)
@@ -269,11 +270,11 @@ def single_launch_floor(byte_counts, qmv_us, dev, stream, reps):
     start = int(lines[0])
 
     def chase_us(h):
-        lb.lowbit_probe_stream_read(buf, ROTATE_BYTES, 4, sink, stream=stream)   # flush caches
+        probe.stream_read(buf, ROTATE_BYTES, 4, sink, stream=stream)   # flush caches
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        lb.lowbit_probe_chase(chain, h, start, out, stream=stream)
+        probe.chase(chain, h, start, out, stream=stream)
         e1.record(stream)
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3

@@ -1,4 +1,5 @@
-"""Build the HIP library liblowbit.so for gfx950, in-tree.
+"""Build the HIP library liblowbit.so (and the benchmark's probe library
+liblowbit_probe.so) for gfx950, in-tree.
 
 Every source is compiled with hipcc for --offload-arch=gfx950 with packed-fp32
 instruction selection disabled.  The quantizer is compiled with
@@ -41,7 +42,6 @@ def hipcc() -> str:
 def _units():
     units = [("lowbit_api.cpp", "lowbit_api.o", []),
              ("quant_pack.hip", "quant_pack.o", ["-ffp-contract=off"]),
-             ("probe.hip", "probe.o", []),
              ("device_scratch.hip", "device_scratch.o", [])]
     for b in range(1, 8):
         units.append(("qmv.hip", f"qmv_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
@@ -49,6 +49,12 @@ def _units():
         units.append(("qmm_bf16.hip", f"qmm_bf16_b{b}.o",
                       [f"-DLOWBIT_BITS={b}", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]))
     return units
+
+
+# the benchmark's measurement probes: their own library, not part of the layer
+PROBE_UNITS = [("probe.hip", "probe.o", [])]
+PROBE_LIB_NAME = "liblowbit_probe.so"
+PROBE_LIB_PATH = os.path.join(PKG, PROBE_LIB_NAME)
 
 
 RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
@@ -83,7 +89,7 @@ def _compile(unit):
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     """Compile every source and link liblowbit.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    units = _units()
+    units = _units() + PROBE_UNITS
     jobs = jobs or min(len(units), max(1, min(16, os.cpu_count() or 4)))
     spills = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -96,13 +102,14 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if spills:
         listing = "\n".join(f"  {k}: {v} bytes/lane" for k, v in sorted(spills.items()))
         raise RuntimeError(f"kernels spill registers to scratch memory:\n{listing}")
-    objs = [os.path.join(BUILD_DIR, u[1]) for u in units]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    for lib, lib_units in ((LIB_PATH, _units()), (PROBE_LIB_PATH, PROBE_UNITS)):
+        objs = [os.path.join(BUILD_DIR, u[1]) for u in lib_units]
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB_PATH
 
 

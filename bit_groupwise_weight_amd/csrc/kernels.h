@@ -11,14 +11,14 @@ enum ActKind : int { ACT_F32 = 0, ACT_F16 = 1, ACT_BF16 = 2 };
 
 // ---------------------------------------------------------------- quantize --
 struct QuantParams {
-  const float* w;      // N x K fp32
+  const void* w;       // N x K, w_act (fp32, fp16 or bf16; upcast exactly to fp32)
   void* scales;        // N x G, sz dtype
   void* zeros;         // N x G, sz dtype
   uint8_t* packed;     // N x K*bits/8
   uint8_t* codes;      // N x K or nullptr
   int* status;         // [0] non-finite weight seen, [1] non-finite stored scale/zero
   int64_t N, K;
-  int bits, group, sz_act;
+  int bits, group, sz_act, w_act;
 };
 hipError_t launch_quant_pack(const QuantParams& p, hipStream_t stream);
 
@@ -146,14 +146,8 @@ constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
 // Device address of this device's copy of the array (looked up once per
 // device, with that device current).
 hipError_t noalloc_scratch(void** out);
-
-// ------------------------------------------------------- measurement probes --
-// Plain streaming read of `bytes` (multiple of 16) with loads_per_thread
-// (1, 2, 4 or 8) 16-byte loads per thread and round.
-hipError_t launch_stream_read(const void* src, int64_t bytes, int loads_per_thread, uint32_t* sink,
-                              hipStream_t s);
-// One lane follows `hops` dependent links of chain[0 .. chain_len) from start.
-hipError_t launch_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
-                        uint32_t* out, hipStream_t s);
+// Device address of this device's two status words of the quantizer (a
+// second library-owned device array, looked up the same way).
+hipError_t quant_status_words(int** out);
 
 }  // namespace lowbit

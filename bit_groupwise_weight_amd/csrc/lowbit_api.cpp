@@ -3,6 +3,7 @@
 // runtime, so every argument error is reported identically with or without a
 // GPU present.
 #include "lowbit.h"
+#include "lowbit_tuning.h"
 
 #include <hip/hip_runtime.h>
 
@@ -78,29 +79,22 @@ lowbit_status check_linear(const void* x, lowbit_dtype act_dtype, const uint8_t*
   return LOWBIT_OK;
 }
 
-// One status word pair per device for lowbit_quantize_pack, allocated on first
-// use and kept for the life of the process.  A call holds its device's mutex
-// from clearing the word until it has read it back, so concurrent calls on
-// one device (from any threads, on any streams) never see each other's flags.
+// The quantizer's status words live in a device array that the library holds
+// on every device (no allocation).  A call holds its device's mutex from
+// clearing the words until it has read them back, so concurrent calls on one
+// device (from any threads, on any streams) never see each other's flags.
 constexpr int kMaxDevices = 64;
 std::mutex g_status_mu[kMaxDevices];
-int* g_status[kMaxDevices] = {};
 
-// Current device and its status word; on success *lock holds that device's
-// mutex.
+// Current device's status words; on success *lock holds that device's mutex.
 lowbit_status device_status_word(int** out, std::unique_lock<std::mutex>* lock) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(LOWBIT_ERR_HIP, "device id %d out of range", dev);
   std::unique_lock<std::mutex> held(g_status_mu[dev]);
-  if (g_status[dev] == nullptr) {
-    void* p = nullptr;
-    e = hipMalloc(&p, 2 * sizeof(int));
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(status)");
-    g_status[dev] = static_cast<int*>(p);
-  }
-  *out = g_status[dev];
+  e = lowbit::quant_status_words(out);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(status)");
   *lock = std::move(held);
   return LOWBIT_OK;
 }
@@ -147,9 +141,13 @@ const QmvStageBytes kQmvStage[8] = {nullptr,
 // LDS budget of one decode block for its staged activations.
 constexpr int64_t kQmvStageBudget = 64 * 1024 - 256;
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
+// Overrides of the automatic schedule choices (lowbit_set_tuning; 0 = none),
+// for tests and benchmarks.  Nothing reads the environment.
+std::atomic<int> g_tuning[LOWBIT_TUNE_COUNT] = {};
+
+int tuning(lowbit_tuning_key key, int dflt) {
+  const int v = g_tuning[key].load(std::memory_order_relaxed);
+  return v != 0 ? v : dflt;
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
@@ -210,7 +208,7 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   if (M >= 3 && 4 * max_per_row <= kQmvStageBudget) l.mt = 4;
   if (max_per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
   // Block size: 256 threads unless that leaves fewer blocks than CUs.
-  int threads = env_int("LOWBIT_QMV_BLOCK", 0);
+  int threads = tuning(LOWBIT_TUNE_QMV_BLOCK, 0);
   auto blocks_for = [&](int t, int i, int variant) {
     const int64_t rows_per_block =
         static_cast<int64_t>(t >> b.prob[i].lpr_shift) * lowbit::qmv_rows_per_group(bits, l.mt, variant);
@@ -254,7 +252,7 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
     l.variant = total_blocks(threads, lowbit::QMV_LEAN2) * by >= 6 * cus ? lowbit::QMV_LEAN2 : lowbit::QMV_LEAN;
   else if (l.mt == 1 && waves < 2 * cus && lowbit::qmv_rows_per_group(bits, 1, lowbit::QMV_DEFAULT) == 2)
     l.variant = lowbit::QMV_LEAN1;
-  const int var_env = env_int("LOWBIT_QMV_VARIANT", -1);   // (tuning and tests: 0..3 forces it)
+  const int var_env = tuning(LOWBIT_TUNE_QMV_VARIANT, 0) - 1;   // (override: 1..4 forces variant 0..3)
   if (l.mt == 1 && var_env >= 0 && var_env <= 3) l.variant = var_env;
   int64_t bx = 0;
   for (int i = 0; i < count; ++i) bx = std::max<int64_t>(bx, blocks_for(threads, i, l.variant));
@@ -296,13 +294,13 @@ struct QmmSchedule {
 // Block tiles and K split for column tile width 16*nt*waves: one block per
 // CU (each block takes a whole CU's register file), K split just enough that
 // the tiles times the splits fill the CUs without a second, partial wave of
-// blocks (LOWBIT_QMM_BLOCKS overrides the block target for tuning).
+// blocks (LOWBIT_TUNE_QMM_BLOCKS overrides the block target).
 void qmm_split(QmmSchedule& sc, int64_t M, int64_t N, int64_t K) {
   const int64_t bn = 16 * sc.nt * sc.waves;
   sc.tiles_n = (N + bn - 1) / bn;
   sc.tiles_m = (M + 16 * sc.mtt - 1) / (16 * sc.mtt);
   sc.ksteps = (K + 127) / 128;
-  const int64_t target = env_int("LOWBIT_QMM_BLOCKS", device_cus());
+  const int64_t target = tuning(LOWBIT_TUNE_QMM_BLOCKS, device_cus());
   const int64_t tiles = sc.tiles_n * sc.tiles_m;
   int64_t s = std::max<int64_t>(1, target / tiles);
   const int64_t max_split = std::max<int64_t>(1, sc.ksteps / 2);   // >= 2 steps per split
@@ -339,7 +337,7 @@ constexpr int kQmmKGroupsMinSteps = 8;
 QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  const int mtt_env = env_int("LOWBIT_QMM_MTT", 0);
+  const int mtt_env = tuning(LOWBIT_TUNE_QMM_MTT, 0);
   if (mtt_env == 1 || mtt_env == 2 || mtt_env == 4 || mtt_env == 8) sc.mtt = std::min(sc.mtt, mtt_env);
   sc.nt = 2;
   if (act == LOWBIT_BF16) {
@@ -359,12 +357,11 @@ QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64
   // per CU than 4-wave blocks at M = 128, K = 4096, N = 14336; the wider tile
   // needs twice the K splits, whose partial planes cost more than that gain
   // once the split exceeds ~4), else 4 waves.
-  // (LOWBIT_QMM_MTT, LOWBIT_QMM_KGROUPS, LOWBIT_QMM_WAVES and LOWBIT_QMM_NT
-  // override the choices for tuning; LOWBIT_QMM_WAVES applies with one K
-  // group, LOWBIT_QMM_NT with two at 128-row tiles.)
+  // (LOWBIT_TUNE_QMM_MTT, _KGROUPS, _WAVES and _NT override the choices;
+  // _WAVES applies with one K group, _NT with two at 128-row tiles.)
   const bool can8 = bits <= lowbit::qmm_max_bits_8waves;
   const bool can_kg = bits <= lowbit::qmm_max_bits_kgroups;
-  const int kg_env = env_int("LOWBIT_QMM_KGROUPS", 0);
+  const int kg_env = tuning(LOWBIT_TUNE_QMM_KGROUPS, 0);
   if (can_kg && kg_env != 1) {
     QmmSchedule kg = sc;
     kg.kgroups = 2;
@@ -373,7 +370,7 @@ QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64
       QmmSchedule narrow = kg;
       narrow.nt = 1;
       qmm_split(narrow, M, N, K);
-      const int nt_env = env_int("LOWBIT_QMM_NT", 0);
+      const int nt_env = tuning(LOWBIT_TUNE_QMM_NT, 0);
       if (nt_env == 1 || (nt_env != 2 && narrow.ksteps_per_split <= kQmmNarrowMaxSteps)) return narrow;
     }
     qmm_split(kg, M, N, K);
@@ -381,7 +378,7 @@ QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64
   }
   sc.kgroups = 1;
   const int wv_default = (can8 && sc.mtt == 8 && (N + 255) / 256 >= device_cus() / 5) ? 8 : 4;
-  sc.waves = (can8 && env_int("LOWBIT_QMM_WAVES", wv_default) == 8) ? 8 : 4;
+  sc.waves = (can8 && tuning(LOWBIT_TUNE_QMM_WAVES, wv_default) == 8) ? 8 : 4;
   qmm_split(sc, M, N, K);
   return sc;
 }
@@ -437,35 +434,6 @@ int64_t lowbit_num_groups(int64_t K, int group) {
   return K / group;
 }
 
-lowbit_status lowbit_probe_stream_read(const void* src, size_t bytes, int loads_per_thread,
-                                       uint32_t* sink, void* stream) {
-  g_last_error.clear();
-  if (!src || !sink) return fail(LOWBIT_ERR_INVALID_ARG, "NULL src or sink");
-  if (bytes == 0 || bytes % 16 != 0 || bytes > (size_t{1} << 40))
-    return fail(LOWBIT_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
-  if (loads_per_thread != 1 && loads_per_thread != 2 && loads_per_thread != 4 && loads_per_thread != 8)
-    return fail(LOWBIT_ERR_INVALID_ARG, "loads_per_thread=%d not one of 1/2/4/8", loads_per_thread);
-  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(LOWBIT_ERR_MISALIGNED, "src/sink alignment");
-  const hipError_t e = lowbit::launch_stream_read(src, static_cast<int64_t>(bytes), loads_per_thread,
-                                                  sink, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? LOWBIT_OK : hip_fail(e, "stream read launch");
-}
-
-lowbit_status lowbit_probe_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
-                                 uint32_t* out, void* stream) {
-  g_last_error.clear();
-  if (!chain || !out) return fail(LOWBIT_ERR_INVALID_ARG, "NULL chain or out");
-  if (chain_len < 1 || chain_len > (int64_t{1} << 32))
-    return fail(LOWBIT_ERR_INVALID_ARG, "chain_len=%lld not in 1..2^32", (long long)chain_len);
-  if (hops < 0 || hops > (1 << 24)) return fail(LOWBIT_ERR_INVALID_ARG, "hops=%d not in 0..2^24", hops);
-  if (static_cast<int64_t>(start) >= chain_len)
-    return fail(LOWBIT_ERR_INVALID_ARG, "start=%u past the chain", start);
-  if (!aligned(chain, 4) || !aligned(out, 4)) return fail(LOWBIT_ERR_MISALIGNED, "chain/out alignment");
-  const hipError_t e = lowbit::launch_chase(chain, chain_len, hops, start, out,
-                                            static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? LOWBIT_OK : hip_fail(e, "chase launch");
-}
-
 const char* lowbit_status_string(lowbit_status s) {
   switch (s) {
     case LOWBIT_OK: return "ok";
@@ -482,12 +450,22 @@ const char* lowbit_status_string(lowbit_status s) {
 
 const char* lowbit_last_error(void) { return g_last_error.c_str(); }
 
-lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t N, int64_t K,
-                                   lowbit_dtype sz_dtype, void* scales, void* zeros,
+lowbit_status lowbit_set_tuning(lowbit_tuning_key key, int value) {
+  g_last_error.clear();
+  if (static_cast<int>(key) < 0 || key >= LOWBIT_TUNE_COUNT)
+    return fail(LOWBIT_ERR_INVALID_ARG, "tuning key %d", (int)key);
+  if (value < 0) return fail(LOWBIT_ERR_INVALID_ARG, "tuning value %d", value);
+  g_tuning[key].store(value, std::memory_order_relaxed);
+  return LOWBIT_OK;
+}
+
+lowbit_status lowbit_quantize_pack(const void* w, lowbit_dtype w_dtype, int bits, int group, int64_t N,
+                                   int64_t K, lowbit_dtype sz_dtype, void* scales, void* zeros,
                                    uint8_t* packed, uint8_t* codes, void* stream) {
   g_last_error.clear();
   lowbit_status st = check_common(bits, group, N, K);
   if (st != LOWBIT_OK) return st;
+  if (!valid_dtype(w_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "w_dtype=%d", (int)w_dtype);
   if (!valid_dtype(sz_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "sz_dtype=%d", (int)sz_dtype);
   if (!w || !scales || !zeros || !packed) return fail(LOWBIT_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(w, 16)) return fail(LOWBIT_ERR_MISALIGNED, "w must be 16-byte aligned");
@@ -507,6 +485,7 @@ lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t 
   p.w = w; p.scales = scales; p.zeros = zeros; p.packed = packed; p.codes = codes;
   p.status = status; p.N = N; p.K = K; p.bits = bits; p.group = group;
   p.sz_act = act_kind(sz_dtype);
+  p.w_act = act_kind(w_dtype);
   he = lowbit::launch_quant_pack(p, s);
   if (he != hipSuccess) return hip_fail(he, "quant_pack launch");
   int host[2] = {0, 0};

@@ -1,12 +1,17 @@
-// Measurement instruments for the decode kernel's roofline: what a plain
+// Measurement instruments for the decode kernel's roofline (the library
+// liblowbit_probe.so, C ABI in include/lowbit_probe.h): what a plain
 // streaming read of the same bytes achieves in one launch, and the latency of
 // one dependent load from HBM.  Neither is part of the layer; the benchmark
 // reports them beside the decode timings, because at decode sizes (a few MB)
 // launch and memory latency, not bandwidth, bound a single kernel.
-#include <algorithm>
+#include <hip/hip_runtime.h>
 
-#include "device_common.h"
-#include "kernels.h"
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "lowbit_probe.h"
 
 namespace lowbit {
 
@@ -67,3 +72,54 @@ hipError_t launch_chase(const uint32_t* chain, int64_t chain_len, int hops, uint
 }
 
 }  // namespace lowbit
+
+namespace {
+thread_local std::string g_probe_error;
+
+lowbit_status probe_fail(lowbit_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lowbit_status probe_fail(lowbit_status st, const char* fmt, ...) {
+  char buf[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_probe_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+}  // namespace
+
+extern "C" {
+
+lowbit_status lowbit_probe_stream_read(const void* src, size_t bytes, int loads_per_thread,
+                                       uint32_t* sink, void* stream) {
+  g_probe_error.clear();
+  if (!src || !sink) return probe_fail(LOWBIT_ERR_INVALID_ARG, "NULL src or sink");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > (size_t{1} << 40))
+    return probe_fail(LOWBIT_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (loads_per_thread != 1 && loads_per_thread != 2 && loads_per_thread != 4 && loads_per_thread != 8)
+    return probe_fail(LOWBIT_ERR_INVALID_ARG, "loads_per_thread=%d not one of 1/2/4/8", loads_per_thread);
+  if (!aligned(src, 16) || !aligned(sink, 4)) return probe_fail(LOWBIT_ERR_MISALIGNED, "src/sink alignment");
+  const hipError_t e = lowbit::launch_stream_read(src, static_cast<int64_t>(bytes), loads_per_thread,
+                                                  sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOWBIT_OK : probe_fail(LOWBIT_ERR_HIP, "stream read launch: %s", hipGetErrorString(e));
+}
+
+lowbit_status lowbit_probe_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
+                                 uint32_t* out, void* stream) {
+  g_probe_error.clear();
+  if (!chain || !out) return probe_fail(LOWBIT_ERR_INVALID_ARG, "NULL chain or out");
+  if (chain_len < 1 || chain_len > (int64_t{1} << 32))
+    return probe_fail(LOWBIT_ERR_INVALID_ARG, "chain_len=%lld not in 1..2^32", (long long)chain_len);
+  if (hops < 0 || hops > (1 << 24)) return probe_fail(LOWBIT_ERR_INVALID_ARG, "hops=%d not in 0..2^24", hops);
+  if (static_cast<int64_t>(start) >= chain_len)
+    return probe_fail(LOWBIT_ERR_INVALID_ARG, "start=%u past the chain", start);
+  if (!aligned(chain, 4) || !aligned(out, 4)) return probe_fail(LOWBIT_ERR_MISALIGNED, "chain/out alignment");
+  const hipError_t e = lowbit::launch_chase(chain, chain_len, hops, start, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOWBIT_OK : probe_fail(LOWBIT_ERR_HIP, "chase launch: %s", hipGetErrorString(e));
+}
+
+const char* lowbit_probe_last_error(void) { return g_probe_error.c_str(); }
+
+}  // extern "C"

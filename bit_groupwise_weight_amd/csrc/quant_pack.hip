@@ -1,4 +1,5 @@
-// Quantize + pack kernel: fp32 weights -> per-(row, group) scale and zero,
+// Quantize + pack kernel: weights (fp32, or fp16 / bf16 upcast exactly to
+// fp32) -> per-(row, group) scale and zero,
 // unsigned b-bit codes and the LSB-first contiguous packed stream.
 //
 // Format (pages "Add torchao mps ops", linear:afpwx description, and
@@ -21,7 +22,26 @@
 
 namespace lowbit {
 
-template <int SZ_ACT>
+// The 8 weights of one atom as fp32 (fp16 and bf16 values are exact in fp32).
+template <int W_ACT>
+__device__ __forceinline__ void load_atom(const void* w, int64_t off, float (&out)[8]) {
+  if constexpr (W_ACT == ACT_F32) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(w) + off);
+    const float4 v0 = src[0], v1 = src[1];
+    out[0] = v0.x; out[1] = v0.y; out[2] = v0.z; out[3] = v0.w;
+    out[4] = v1.x; out[5] = v1.y; out[6] = v1.z; out[7] = v1.w;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + off);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = act_bits_to_float<W_ACT>(d[i] & 0xFFFFu);
+      out[2 * i + 1] = act_bits_to_float<W_ACT>(d[i] >> 16);
+    }
+  }
+}
+
+template <int SZ_ACT, int W_ACT>
 __global__ __launch_bounds__(256) void quant_pack_kernel(QuantParams p) {
   const int64_t atoms_per_row = p.K >> 3;
   const int64_t total = p.N * atoms_per_row;
@@ -33,12 +53,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(QuantParams p) {
   const int seg = p.group >> 3;           // threads per group: 4, 8, 16 or 32
 
   float w[8];
-  {
-    const float4* src = reinterpret_cast<const float4*>(p.w + n * p.K + a * 8);
-    float4 v0 = src[0], v1 = src[1];
-    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-  }
+  load_atom<W_ACT>(p.w, n * p.K + a * 8, w);
   bool finite = true;
   float mn = w[0], mx = w[0];
 #pragma unroll
@@ -108,10 +123,17 @@ hipError_t launch_quant_pack(const QuantParams& p, hipStream_t stream) {
   const int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(threads);
-  switch (p.sz_act) {
-    case ACT_F32: quant_pack_kernel<ACT_F32><<<grid, block, 0, stream>>>(p); break;
-    case ACT_F16: quant_pack_kernel<ACT_F16><<<grid, block, 0, stream>>>(p); break;
-    case ACT_BF16: quant_pack_kernel<ACT_BF16><<<grid, block, 0, stream>>>(p); break;
+  if (p.sz_act < ACT_F32 || p.sz_act > ACT_BF16) return hipErrorInvalidValue;
+  switch (p.w_act * 3 + p.sz_act) {
+    case ACT_F32 * 3 + ACT_F32: quant_pack_kernel<ACT_F32, ACT_F32><<<grid, block, 0, stream>>>(p); break;
+    case ACT_F32 * 3 + ACT_F16: quant_pack_kernel<ACT_F16, ACT_F32><<<grid, block, 0, stream>>>(p); break;
+    case ACT_F32 * 3 + ACT_BF16: quant_pack_kernel<ACT_BF16, ACT_F32><<<grid, block, 0, stream>>>(p); break;
+    case ACT_F16 * 3 + ACT_F32: quant_pack_kernel<ACT_F32, ACT_F16><<<grid, block, 0, stream>>>(p); break;
+    case ACT_F16 * 3 + ACT_F16: quant_pack_kernel<ACT_F16, ACT_F16><<<grid, block, 0, stream>>>(p); break;
+    case ACT_F16 * 3 + ACT_BF16: quant_pack_kernel<ACT_BF16, ACT_F16><<<grid, block, 0, stream>>>(p); break;
+    case ACT_BF16 * 3 + ACT_F32: quant_pack_kernel<ACT_F32, ACT_BF16><<<grid, block, 0, stream>>>(p); break;
+    case ACT_BF16 * 3 + ACT_F16: quant_pack_kernel<ACT_F16, ACT_BF16><<<grid, block, 0, stream>>>(p); break;
+    case ACT_BF16 * 3 + ACT_BF16: quant_pack_kernel<ACT_BF16, ACT_BF16><<<grid, block, 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

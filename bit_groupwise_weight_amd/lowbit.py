@@ -31,9 +31,12 @@ _ENUM_DTYPE = {v: k for k, v in _DTYPE_ENUM.items()}
 EXPORTED_SYMBOLS = (
     "lowbit_abi_version", "lowbit_packed_bytes", "lowbit_num_groups", "lowbit_quantize_pack",
     "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path", "lowbit_linear_multi",
-    "lowbit_status_string", "lowbit_last_error", "lowbit_probe_stream_read", "lowbit_probe_chase",
-    "lowbit_linear_noalloc",
+    "lowbit_status_string", "lowbit_last_error", "lowbit_linear_noalloc", "lowbit_set_tuning",
 )
+ABI_VERSION = 2
+# schedule overrides (include/lowbit_tuning.h)
+TUNE_KEYS = {"qmv_block": 0, "qmv_variant": 1, "qmm_blocks": 2, "qmm_mtt": 3, "qmm_kgroups": 4,
+             "qmm_nt": 5, "qmm_waves": 6}
 MAX_MULTI = 8   # LOWBIT_MAX_MULTI
 
 
@@ -76,8 +79,8 @@ def load() -> ctypes.CDLL:
     lib.lowbit_num_groups.restype = c_i64
     lib.lowbit_num_groups.argtypes = [c_i64, ctypes.c_int]
     lib.lowbit_quantize_pack.restype = ctypes.c_int
-    lib.lowbit_quantize_pack.argtypes = [vp, ctypes.c_int, ctypes.c_int, c_i64, c_i64, ctypes.c_int,
-                                         vp, vp, vp, vp, vp]
+    lib.lowbit_quantize_pack.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, c_i64, c_i64,
+                                         ctypes.c_int, vp, vp, vp, vp, vp]
     lib.lowbit_linear_workspace_bytes.restype = c_sz
     lib.lowbit_linear_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, c_i64, c_i64, c_i64,
                                                   ctypes.c_int]
@@ -96,10 +99,11 @@ def load() -> ctypes.CDLL:
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_last_error.restype = ctypes.c_char_p
     lib.lowbit_last_error.argtypes = []
-    lib.lowbit_probe_stream_read.restype = ctypes.c_int
-    lib.lowbit_probe_stream_read.argtypes = [vp, c_sz, ctypes.c_int, vp, vp]
-    lib.lowbit_probe_chase.restype = ctypes.c_int
-    lib.lowbit_probe_chase.argtypes = [vp, c_i64, ctypes.c_int, ctypes.c_uint32, vp, vp]
+    lib.lowbit_set_tuning.restype = ctypes.c_int
+    lib.lowbit_set_tuning.argtypes = [ctypes.c_int, ctypes.c_int]
+    if lib.lowbit_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.lowbit_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it with __graft_entry__.build()")
     _lib = lib
     return lib
 
@@ -216,13 +220,14 @@ def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch
                          want_codes: bool = False, out: Optional[Tuple] = None,
                          stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor,
                                                Optional[torch.Tensor]]:
-    """Quantize fp32 w[N, K] on the GPU.  Returns (packed, scales, zeros, codes|None).
+    """Quantize w[N, K] (fp32, or fp16 / bf16 taken exactly as fp32) on the GPU.
+    Returns (packed, scales, zeros, codes|None).
 
     `out` may give preallocated (packed, scales, zeros, codes) tensors.
     """
     lib = load()
     _expect(w.dim() == 2, "w must be 2-D [N, K]")
-    _expect(w.dtype == torch.float32, f"w must be float32, got {w.dtype}")
+    _expect(w.dtype in _DTYPE_ENUM, f"w must be float32, float16 or bfloat16, got {w.dtype}")
     _expect(sz_dtype in _DTYPE_ENUM, f"sz_dtype {sz_dtype} is not float32, float16 or bfloat16")
     N, K = w.shape
     if out is None:
@@ -242,7 +247,8 @@ def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch
         _expect(tuple(codes.shape) == (N, K) and codes.dtype == torch.uint8, f"codes must be [{N}, {K}] uint8")
     _require_cuda(w, packed, scales, zeros, codes)
     with torch.cuda.device(w.device):
-        st = lib.lowbit_quantize_pack(_ptr(w), bits, group, N, K, _DTYPE_ENUM[sz_dtype], _ptr(scales),
+        st = lib.lowbit_quantize_pack(_ptr(w), _DTYPE_ENUM[w.dtype], bits, group, N, K,
+                                      _DTYPE_ENUM[sz_dtype], _ptr(scales),
                                       _ptr(zeros), _ptr(packed), _ptr(codes),
                                       _stream_handle(w.device, stream))
     _check(st, "lowbit_quantize_pack")
@@ -250,8 +256,13 @@ def lowbit_quantize_pack(w: torch.Tensor, bits: int, group: int, sz_dtype: torch
 
 
 # Workspaces kept per (device, stream): calls on one stream run in order, so
-# they never use the same workspace at the same time.
+# they never use the same workspace at the same time.  A buffer handed out
+# once is never freed: a HIP graph captured over a call keeps its address and
+# writes to it on every replay, so when a larger workspace is needed the old
+# one is retired (kept alive), not released.  Sizes grow by powers of two, so
+# the retired buffers add up to less than the current one.
 _workspaces = {}
+_retired_workspaces = []
 
 
 def cached_workspace(device: torch.device, stream_handle, nbytes: int) -> Optional[torch.Tensor]:
@@ -261,7 +272,10 @@ def cached_workspace(device: torch.device, stream_handle, nbytes: int) -> Option
     key = (device.index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if ws is not None:
+            _retired_workspaces.append(ws)
+        size = 1 << max(20, (nbytes - 1).bit_length())
+        ws = torch.empty(size, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -348,32 +362,26 @@ def lowbit_linear_multi(items, bits: int, group: int, stream=None):
     return outs
 
 
-# ---------------------------------------------------------------- probes --
-# Measurement instruments of the library (not part of the layer): a plain
-# streaming read and a dependent-load chain, used by the benchmark to report
-# the decode kernel against the single-launch floor of the device.
+# ----------------------------------------------------------------- tuning --
 
-def lowbit_probe_stream_read(src: torch.Tensor, nbytes: int, loads_per_thread: int,
-                             sink: torch.Tensor, stream=None) -> None:
-    """Read the first nbytes of src (device) with plain 16-byte loads in one launch."""
-    lib = load()
-    _require_cuda(src, sink)
-    _expect(nbytes <= src.numel() * src.element_size(), "nbytes exceeds src")
-    _expect(sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1, "sink: one 32-bit word")
-    with torch.cuda.device(src.device):
-        st = lib.lowbit_probe_stream_read(_ptr(src), nbytes, loads_per_thread, _ptr(sink),
-                                          _stream_handle(src.device, stream))
-    _check(st, "lowbit_probe_stream_read")
+def lowbit_set_tuning(key: str, value: int) -> None:
+    """Set (value > 0) or clear (0) a schedule override (tests and benchmarks)."""
+    _check(load().lowbit_set_tuning(TUNE_KEYS[key], int(value)), "lowbit_set_tuning")
 
 
-def lowbit_probe_chase(chain: torch.Tensor, hops: int, start: int, out: torch.Tensor,
-                       stream=None) -> None:
-    """Follow hops dependent links i <- chain[i] (int32/uint32 device array) from start."""
-    lib = load()
-    _require_cuda(chain, out)
-    _expect(chain.dtype in (torch.int32, torch.uint32) and chain.is_contiguous(), "chain: 32-bit, contiguous")
-    _expect(out.dtype in (torch.int32, torch.uint32) and out.numel() >= 1, "out: one 32-bit word")
-    with torch.cuda.device(chain.device):
-        st = lib.lowbit_probe_chase(_ptr(chain), chain.numel(), hops, start, _ptr(out),
-                                    _stream_handle(chain.device, stream))
-    _check(st, "lowbit_probe_chase")
+class tuning:
+    """Context manager: schedule overrides for the calls inside it, e.g.
+    `with lowbit.tuning(qmm_nt=1, qmm_kgroups=2): ...`; cleared on exit."""
+
+    def __init__(self, **overrides: int):
+        self.overrides = overrides
+
+    def __enter__(self):
+        for k, v in self.overrides.items():
+            lowbit_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k in self.overrides:
+            lowbit_set_tuning(k, 0)
+        return False

@@ -72,7 +72,11 @@ def quantize_pack(w: torch.Tensor, bits: int, group: int,
     _check_bits_group(bits, group)
     if sz_dtype not in _SZ_DTYPES:
         raise ValueError(f"sz_dtype must be one of {_SZ_DTYPES}")
-    packed, scales, zeros, _ = _lb.lowbit_quantize_pack(w.float().contiguous(), bits, group, sz_dtype)
+    # fp32, fp16 and bf16 weights go in as they are (the kernel takes fp16 and
+    # bf16 values exactly as fp32); other dtypes are converted to fp32 first
+    if w.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        w = w.float()
+    packed, scales, zeros, _ = _lb.lowbit_quantize_pack(w.contiguous(), bits, group, sz_dtype)
     return packed, scales, zeros
 
 

@@ -33,8 +33,11 @@
  *
  * Memory: every pointer argument other than `stream` and the host-side helpers
  * is a DEVICE pointer owned by the caller; the library never keeps a pointer
- * after a call returns.  The library allocates one small per-device status
- * word for lowbit_quantize_pack on first use and nothing else.
+ * after a call returns.  The library allocates no device memory: it holds,
+ * on every device it runs on, two small arrays of its own (the quantizer's
+ * status words and the scratch of lowbit_linear_noalloc).  Measurement
+ * probes live in a separate library (lowbit_probe.h); schedule overrides
+ * for tests and benchmarks in lowbit_tuning.h.
  *
  * Errors: arguments are validated on the host before any HIP call, so every
  * LOWBIT_ERR_INVALID_ARG / UNSUPPORTED / MISALIGNED / WORKSPACE result can be
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 1
+#define LOWBIT_ABI_VERSION 2
 
 typedef enum lowbit_status {
   LOWBIT_OK = 0,
@@ -93,7 +96,10 @@ int64_t lowbit_num_groups(int64_t K, int group);
 
 /* Quantize and pack a weight matrix (one-off, not on the decode path).
  *
- *   w        device, fp32, N x K row-major (the linear weight, [out, in]).
+ *   w        device, N x K row-major (the linear weight, [out, in]), 16-byte
+ *            aligned.
+ *   w_dtype  dtype of w: fp32, or fp16 / bf16, whose values are taken exactly
+ *            as fp32 (every fp16 and bf16 value is an fp32 value).
  *   bits     1..7;  group: 32, 64, 128 or 256;  K % group == 0;  N, K > 0.
  *   sz_dtype storage dtype of scales and zeros; use the activation dtype that
  *            lowbit_linear will be called with.
@@ -111,8 +117,8 @@ int64_t lowbit_num_groups(int64_t K, int group);
  * Calls from several threads are safe; on one device they run one at a time
  * (they share the device's status word).  Not for use under stream capture
  * (it waits for the stream). */
-lowbit_status lowbit_quantize_pack(const float* w, int bits, int group, int64_t N, int64_t K,
-                                   lowbit_dtype sz_dtype, void* scales, void* zeros,
+lowbit_status lowbit_quantize_pack(const void* w, lowbit_dtype w_dtype, int bits, int group, int64_t N,
+                                   int64_t K, lowbit_dtype sz_dtype, void* scales, void* zeros,
                                    uint8_t* packed, uint8_t* codes, void* stream);
 
 /* Bytes of workspace that lowbit_linear / lowbit_linear_path can use for the
@@ -209,29 +215,6 @@ typedef struct lowbit_linear_desc {
  * on each desc.  Enqueued on `stream`; asynchronous. */
 lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lowbit_dtype act_dtype,
                                   int bits, int group, int64_t M, void* stream);
-
-/* ---- Measurement instruments (not part of the layer) ----
- * The decode kernel reads a few MB per call, where launch and memory latency
- * rather than bandwidth bound any single kernel.  These two calls measure
- * that floor on the running device so a benchmark can report the decode
- * kernel against it.
- *
- * lowbit_probe_stream_read: reads `bytes` (a positive multiple of 16, src
- * 16-byte aligned) from device memory with plain 16-byte loads,
- * loads_per_thread (1, 2, 4 or 8) per thread per round, in one launch of
- * 256-thread blocks, and discards the data (`sink`, one device word, is
- * written only if the data fold to a fixed constant).  Enqueued on `stream`.
- *
- * lowbit_probe_chase: one lane follows `hops` (0 .. 2^24) dependent links
- * i <- chain[i] of the device array chain[0 .. chain_len) from index
- * `start`, each link clamped to chain_len - 1 (any contents are safe), and
- * writes the final index to the device word `out`.  With links that point
- * to distinct cache lines outside every cache, the time per hop is the
- * latency of one load from HBM.  Enqueued on `stream`. */
-lowbit_status lowbit_probe_stream_read(const void* src, size_t bytes, int loads_per_thread,
-                                       uint32_t* sink, void* stream);
-lowbit_status lowbit_probe_chase(const uint32_t* chain, int64_t chain_len, int hops, uint32_t start,
-                                 uint32_t* out, void* stream);
 
 /* Static text for a status code. */
 const char* lowbit_status_string(lowbit_status status);

@@ -7,28 +7,42 @@ import re
 import pytest
 
 from bit_groupwise_weight_amd import lowbit as lb
+from bit_groupwise_weight_amd import probe
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "lowbit.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADERS = {"lowbit": ["lowbit.h", "lowbit_tuning.h"], "probe": ["lowbit_probe.h"]}
 
 OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 6
 F32, F16, BF16 = 0, 1, 2
 A = 0x10000          # a fake, 256-byte aligned "device" address: never dereferenced
 
 
-def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lowbit_[a-z_0-9]+)\s*\(", src)))
+def declared_functions(lib="lowbit"):
+    names = set()
+    for h in HEADERS[lib]:
+        src = open(os.path.join(INCLUDE, h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(lowbit_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
     assert declared_functions() == sorted(lb.EXPORTED_SYMBOLS)
+    assert declared_functions("probe") == sorted(probe.EXPORTED_SYMBOLS)
 
 
 def test_library_exports_every_declared_symbol(lowbit_lib):
     for name in declared_functions():
         assert hasattr(lowbit_lib, name), name
-    assert lowbit_lib.lowbit_abi_version() == 1
+    assert lowbit_lib.lowbit_abi_version() == 2
+    plib = probe.load()
+    for name in declared_functions("probe"):
+        assert hasattr(plib, name), name
+
+
+def test_probes_are_not_in_the_layer_library(lowbit_lib):
+    assert not hasattr(lowbit_lib, "lowbit_probe_stream_read")
+    assert not hasattr(lowbit_lib, "lowbit_probe_chase")
 
 
 def test_size_helpers(lowbit_lib):
@@ -114,14 +128,30 @@ def test_qmm_path_rejects_fp32(lowbit_lib):
 @pytest.mark.parametrize("args,status", [
     (dict(bits=9), INVALID), (dict(group=100), INVALID), (dict(K=48, group=32), INVALID),
     (dict(w=None), INVALID), (dict(packed=A + 4), MISALIGNED), (dict(w=A + 4), MISALIGNED),
-    (dict(sz=5), UNSUPPORTED), (dict(N=-3), INVALID),
+    (dict(sz=5), UNSUPPORTED), (dict(N=-3), INVALID), (dict(wd=3), UNSUPPORTED),
+    (dict(wd=F16, w=A + 8), MISALIGNED),
 ])
 def test_quantize_validation(lowbit_lib, args, status):
-    a = dict(w=A, bits=4, group=32, N=8, K=64, sz=F16, scales=A, zeros=A, packed=A, codes=None)
+    a = dict(w=A, wd=F32, bits=4, group=32, N=8, K=64, sz=F16, scales=A, zeros=A, packed=A, codes=None)
     a.update(args)
-    st = lowbit_lib.lowbit_quantize_pack(a["w"], a["bits"], a["group"], a["N"], a["K"], a["sz"],
-                                         a["scales"], a["zeros"], a["packed"], a["codes"], None)
+    st = lowbit_lib.lowbit_quantize_pack(a["w"], a["wd"], a["bits"], a["group"], a["N"], a["K"],
+                                         a["sz"], a["scales"], a["zeros"], a["packed"], a["codes"], None)
     assert st == status
+
+
+def test_tuning_validation(lowbit_lib):
+    assert lowbit_lib.lowbit_set_tuning(7, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(-1, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(0, -2) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(3, 0) == OK
+
+
+def test_library_reads_no_environment():
+    """Schedule choices come from the shape and the device only."""
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--undefined-only", lb.library_path()], capture_output=True,
+                          text=True).stdout
+    assert " getenv" not in syms and "secure_getenv" not in syms
 
 
 def test_status_strings(lowbit_lib):
@@ -142,7 +172,7 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     ((A, 1000, 4, A), INVALID), ((A, 1024, 3, A), INVALID), ((A + 8, 1024, 4, A), MISALIGNED),
     ((A, 1024, 4, A + 2), MISALIGNED)])
 def test_probe_stream_read_validation(lowbit_lib, args, status):
-    assert lowbit_lib.lowbit_probe_stream_read(*args, None) == status
+    assert probe.load().lowbit_probe_stream_read(*args, None) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -150,7 +180,7 @@ def test_probe_stream_read_validation(lowbit_lib, args, status):
     ((A, 16, -1, 0, A), INVALID), ((A, 16, (1 << 24) + 1, 0, A), INVALID), ((A, 16, 4, 16, A), INVALID),
     ((A + 2, 16, 4, 0, A), MISALIGNED), ((A, 16, 4, 0, A + 1), MISALIGNED)])
 def test_probe_chase_validation(lowbit_lib, args, status):
-    assert lowbit_lib.lowbit_probe_chase(*args, None) == status
+    assert probe.load().lowbit_probe_chase(*args, None) == status
 
 
 @pytest.mark.parametrize("M,K,N,bits,group,dtype,planes", [

@@ -98,7 +98,7 @@ def test_quantize_refuses_bad_outputs_and_input():
     with pytest.raises(ValueError, match="codes must be"):
         lb.lowbit_quantize_pack(w, BITS, GROUP, torch.float16,
                                 out=(packed, scales, zeros, torch.zeros(N, K - 1, dtype=torch.uint8)))
-    with pytest.raises(ValueError, match="w must be float32"):
-        lb.lowbit_quantize_pack(w.half(), BITS, GROUP, torch.float16)
+    with pytest.raises(ValueError, match="w must be float32, float16 or bfloat16"):
+        lb.lowbit_quantize_pack(w.double(), BITS, GROUP, torch.float16)
     with pytest.raises(ValueError, match="GPU memory"):
         lb.lowbit_quantize_pack(w, BITS, GROUP, torch.float16, out=(packed, scales, zeros, None))

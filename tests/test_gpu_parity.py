@@ -92,6 +92,23 @@ def test_quantize_edge_values(act):
     assert_quant_equal(ref, packed, s, z, codes, bits)
 
 
+@pytest.mark.parametrize("w_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("sz", ["f32", "f16", "bf16"])
+def test_quantize_half_precision_weights(w_dtype, sz):
+    """fp16 / bf16 weights are taken exactly as fp32 (every such value is an
+    fp32 value): bit-exact against the oracle on the upcast weights, for
+    every storage dtype of the scales and zeros."""
+    rng = np.random.default_rng(17)
+    for bits, group, N, K in [(4, 64, 37, 512), (3, 32, 9, 96), (7, 256, 20, 768)]:
+        W = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+        Wh = W.to(TORCH_ACT[w_dtype])
+        ref = oracle.quantize(Wh.float().numpy(), bits, group, sz)
+        packed, s, z, codes = lb.lowbit_quantize_pack(Wh.to(DEV), bits, group, TORCH_ACT[sz],
+                                                      want_codes=True)
+        torch.cuda.synchronize()
+        assert_quant_equal(ref, packed, s, z, codes, bits)
+
+
 def test_quantize_errors():
     W = torch.zeros(4, 64)
     W[2, 5] = float("nan")
@@ -182,7 +199,7 @@ def test_qmm_small(bits, act):
 
 @pytest.mark.parametrize("act", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("bits", range(1, 8))
-def test_qmv_register_variants(bits, act, monkeypatch):
+def test_qmv_register_variants(bits, act):
     """The decode-kernel variants for one activation row (the default, the
     register-lean one, and the lean ones with two or one rows per lane group,
     chosen by blocks and waves per CU) on ragged shapes: each matches the oracle, and all
@@ -196,10 +213,10 @@ def test_qmv_register_variants(bits, act, monkeypatch):
         y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], group, bias_values(b))
         packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, act)
         outs = []
-        for variant in ("0", "1", "2", "3"):
-            monkeypatch.setenv("LOWBIT_QMV_VARIANT", variant)
-            y = lb.lowbit_linear(x.to(DEV), packed, s, z, None if b is None else b.to(DEV), bits, group,
-                                 path=lb.PATH_QMV)
+        for variant in (0, 1, 2, 3):
+            with lb.tuning(qmv_variant=variant + 1):
+                y = lb.lowbit_linear(x.to(DEV), packed, s, z, None if b is None else b.to(DEV), bits,
+                                     group, path=lb.PATH_QMV)
             torch.cuda.synchronize()
             check_close(y, y_ref, A, f"variant={variant} N={N} K={K} b={bits} g={group} {act}")
             outs.append(y)
@@ -210,22 +227,20 @@ def test_qmv_register_variants(bits, act, monkeypatch):
 @pytest.mark.parametrize("waves,kgroups,nt", [("4", "1", "2"), ("8", "1", "2"), ("4", "2", "2"),
                                                ("4", "2", "1")])
 @pytest.mark.parametrize("bits", [1, 3, 4, 5, 7])
-def test_qmm_block_variants(bits, waves, kgroups, nt, monkeypatch):
+def test_qmm_block_variants(bits, waves, kgroups, nt):
     """Every MFMA block shape (4 waves x 128 columns; 8 waves x 256 columns;
     4 column waves x 2 K groups over 128 or 64 columns) on ragged shapes: rows
     past M, columns past N, a last K step of 32, an odd step count (17) so
     that one K group gets a step past the block's range.  8-wave instances
     exist up to 5 bits and K-group instances up to 4; above, the 4-wave kernel
     runs."""
-    monkeypatch.setenv("LOWBIT_QMM_WAVES", waves)
-    monkeypatch.setenv("LOWBIT_QMM_KGROUPS", kgroups)
-    monkeypatch.setenv("LOWBIT_QMM_NT", nt)
-    for (M, N, K, group, bias) in [(128, 300, 416, 32, True), (100, 520, 1024, 64, False),
-                                   (77, 257, 2080, 32, True), (128, 130, 2176, 128, False)]:
-        run_small_linear(M, N, K, bits, group, "bf16", bias, lb.PATH_QMM, seed=bits + N)
+    with lb.tuning(qmm_waves=int(waves), qmm_kgroups=int(kgroups), qmm_nt=int(nt)):
+        for (M, N, K, group, bias) in [(128, 300, 416, 32, True), (100, 520, 1024, 64, False),
+                                       (77, 257, 2080, 32, True), (128, 130, 2176, 128, False)]:
+            run_small_linear(M, N, K, bits, group, "f16", bias, lb.PATH_QMM, seed=bits + N)
 
 
-# (M, N, K, group, bias, blocks): LOWBIT_QMM_BLOCKS sets the block target
+# (M, N, K, group, bias, blocks): the qmm_blocks override sets the block target
 # from which the schedule derives the K split (2 to 8 splits here; 0 = the
 # default target).
 SPLIT_SUM_CASES = [(128, 520, 2048, 64, True, 16), (100, 300, 4096, 128, False, 24),
@@ -235,10 +250,14 @@ SPLIT_SUM_CASES = [(128, 520, 2048, 64, True, 16), (100, 300, 4096, 128, False, 
 
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [2, 4, 5])
-def test_qmm_forced_k_splits(bits, act, monkeypatch):
+def test_qmm_forced_k_splits(bits, act):
     """K splits of 2 to 8 planes, from a workspace filled with garbage: within
     tolerance of the oracle and bitwise equal on a repeated call."""
-    monkeypatch.setenv("LOWBIT_QMM_NT", "2")    # the split counts above assume 2 column tiles
+    with lb.tuning(qmm_nt=2):    # the split counts above assume 2 column tiles
+        _forced_k_splits(bits, act)
+
+
+def _forced_k_splits(bits, act):
     for (M, N, K, group, bias, blocks) in SPLIT_SUM_CASES:
         case = Case("ss", M, K, N, bits, group, act, bias=bias, seed=bits + N + K)
         W = weight_for(case).numpy()
@@ -248,14 +267,12 @@ def test_qmm_forced_k_splits(bits, act, monkeypatch):
         y_ref, A = oracle.linear(x_values(x), ref["q"], ref["s"], ref["z"], group, bias_values(b))
         packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, act)
         xd, bd = x.to(DEV), None if b is None else b.to(DEV)
-        if blocks:
-            monkeypatch.setenv("LOWBIT_QMM_BLOCKS", str(blocks))
-        need = lb.lowbit_linear_workspace_bytes(bits, group, M, N, K, TORCH_ACT[act])
-        assert need > 0, "the case must take a K split"
-        ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
-        y1 = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws, path=lb.PATH_QMM)
-        y2 = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws, path=lb.PATH_QMM)
-        monkeypatch.delenv("LOWBIT_QMM_BLOCKS", raising=False)
+        with lb.tuning(qmm_blocks=blocks):
+            need = lb.lowbit_linear_workspace_bytes(bits, group, M, N, K, TORCH_ACT[act])
+            assert need > 0, "the case must take a K split"
+            ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+            y1 = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws, path=lb.PATH_QMM)
+            y2 = lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws, path=lb.PATH_QMM)
         torch.cuda.synchronize()
         what = f"M={M} N={N} K={K} b={bits} g={group} {act}"
         check_close(y1, y_ref, A, "K split " + what)
@@ -293,6 +310,52 @@ def test_qmm_split_graph_replays():
         assert torch.equal(y, y_eager), f"graph replay {i} differs from the eager call"
         lb.lowbit_linear(xd, packed, s, z, bd, bits, group, workspace=ws)   # eager work between
         torch.cuda.synchronize()
+
+
+def test_cached_workspace_survives_a_larger_call_between_graph_replays():
+    """A graph captured over a call that took the binding's cached workspace
+    keeps that buffer's address; a later, larger call on the same stream
+    needs a bigger workspace.  The old buffer must stay alive: every replay
+    after the larger call still matches the eager result bit for bit."""
+    bits, group, act = 4, 128, "bf16"
+    small = Case("ws_small", 128, 2048, 1024, bits, group, act, bias=True, seed=21)
+    large = Case("ws_large", 128, 8192, 8192, bits, group, act, bias=False, seed=22)
+    side = torch.cuda.Stream()
+
+    def prepared(case):
+        W = weight_for(case).numpy()
+        ref = oracle.quantize(W, bits, group, act)
+        packed, s, z = upload_quant(ref["q"], ref["s"], ref["z"], bits, act)
+        b = make_bias(case)
+        return make_x(case).to(DEV), packed, s, z, None if b is None else b.to(DEV)
+
+    xs, ps, ss, zs, bs = prepared(small)
+    xl, pl, sl, zl, bl = prepared(large)
+    need_s = lb.lowbit_linear_workspace_bytes(bits, group, small.M, small.N, small.K, torch.bfloat16)
+    need_l = lb.lowbit_linear_workspace_bytes(bits, group, large.M, large.N, large.K, torch.bfloat16)
+    assert 0 < need_s < need_l, (need_s, need_l)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y_eager = lb.lowbit_linear(xs, ps, ss, zs, bs, bits, group)       # takes the cached workspace
+        side.synchronize()
+        y = torch.empty_like(y_eager)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            lb.lowbit_linear(xs, ps, ss, zs, bs, bits, group, y=y)
+        side.synchronize()
+        lb.lowbit_linear(xl, pl, sl, zl, bl, bits, group)                # needs a larger workspace
+        side.synchronize()
+        # memory handed out after the resize (the allocator would reuse a freed
+        # workspace block for these sizes) must not be written by the replays
+        sizes = [need_s, 1 << (need_s - 1).bit_length(), 1 << 20]
+        sentinels = [torch.full((n,), 0x3C, dtype=torch.uint8, device=DEV) for n in sizes]
+        for i in range(3):
+            y.fill_(float("nan"))
+            g.replay()
+            side.synchronize()
+            assert torch.equal(y, y_eager), f"replay {i} after a larger call differs"
+            for t in sentinels:
+                assert bool((t == 0x3C).all()), f"replay {i} wrote into memory it does not own"
 
 
 @pytest.mark.parametrize("act", ["f16", "bf16"])

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from bit_groupwise_weight_amd import lowbit as lb
+from bit_groupwise_weight_amd import probe
 from tests.gpu_helpers import DEV
 
 pytestmark = [pytest.mark.gpu,
@@ -32,7 +33,7 @@ def test_chase_matches_host(hops):
     chain = rng.integers(0, n, size=n, dtype=np.int64).astype(np.uint32)
     chain[::17] = np.uint32(0xFFFFFFF0)          # out-of-range links are clamped
     out = torch.zeros(1, dtype=torch.int32, device=DEV)
-    lb.lowbit_probe_chase(torch.from_numpy(chain.view(np.int32)).to(DEV), hops, 5, out)
+    probe.chase(torch.from_numpy(chain.view(np.int32)).to(DEV), hops, 5, out)
     torch.cuda.synchronize()
     assert int(out.item()) == host_chase(chain, hops, 5)
 
@@ -42,6 +43,6 @@ def test_chase_matches_host(hops):
 def test_stream_read_runs(nbytes, lpt):
     src = torch.zeros(nbytes + 256, dtype=torch.uint8, device=DEV)
     sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
-    lb.lowbit_probe_stream_read(src, nbytes, lpt, sink)
+    probe.stream_read(src, nbytes, lpt, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7       # zeros fold to 0, not the constant
