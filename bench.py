@@ -37,6 +37,8 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
+from bit_groupwise_weight_amd import probe  # noqa: E402
+
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 ROTATE_BYTES = 1 << 30
@@ -89,6 +91,13 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a kernel of known "
                          "traffic, to scale hardware byte counters)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="after the timed steps, time every workload configuration (127 cases, "
+                         "each with its own rotation) and the single-launch floor at the wide "
+                         "decode shapes; adds the field all_configs (not part of value)")
+    ap.add_argument("--only-configs", default="",
+                    help="with --all-configs: comma-separated workload keys to run (single, "
+                         "llama8b, llama_small, batched, mixed); default all")
     return ap.parse_args()
 
 
@@ -115,7 +124,6 @@ def algo_bytes(case) -> int:
 def prepare(case, copies, dev):
     """Quantize once on the GPU and make `copies` independent copies of the weights."""
     from bit_groupwise_weight_amd import lowbit as lb
-from bit_groupwise_weight_amd import probe
     from bit_groupwise_weight_amd.workloads import make_bias, make_weight, make_x
     act = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.act]
     W = make_weight(case).to(dev)
@@ -231,6 +239,34 @@ def layer_fused(L, i, stream):
     lb.lowbit_linear_multi([item("down", 14336)], LAYER_BITS, LAYER_GROUP, stream=stream)
 
 
+def plain_read_us(byte_counts, dev, stream, reps):
+    """Per byte count: the best (microseconds, loads per thread) of a plain
+    16-byte streaming read of that many bytes in one launch, rotating over
+    >= 1 GiB, graph-timed."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    buf = torch.empty(ROTATE_BYTES + (64 << 20), dtype=torch.uint8, device=dev)
+    out = []
+    for nb in byte_counts:
+        nb16 = (nb + 15) // 16 * 16
+        slot = (nb16 + 4095) // 4096 * 4096
+        n = max(2, ROTATE_BYTES // slot)
+        best = None
+        for lpt in (1, 2, 4, 8):
+            def fn(i, s, lpt=lpt):
+                probe.stream_read(buf[(i % n) * slot:], nb16, lpt, sink, stream=s)
+            for i in range(3):
+                fn(i, stream)
+            g = capture(fn, n, stream)
+            us = time_graph(g, max(1, reps // n + 1), n, stream)
+            del g
+            if best is None or us < best[0]:
+                best = (us, lpt)
+        out.append(best)
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def single_launch_floor(byte_counts, qmv_us, dev, stream, reps):
     """The device's floor for one kernel that reads a few MB: a plain
     streaming read of each byte count in one launch, rotating over >= 1 GiB
@@ -309,33 +345,148 @@ def single_launch_floor(byte_counts, qmv_us, dev, stream, reps):
                     "summed over bits 1..7"}
 
 
-def cpu_baseline(cases, reps):
-    """The CPU oracle's linear (fp64 dequant + matmul) timed on this host."""
+def host_cpu():
+    """This host's CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return model, nproc
+
+
+def cpu_baseline(cases, reps, single_reps=3):
+    """The CPU oracle's linear (fp64 dequant + matmul) timed on this host: on
+    all the threads its BLAS uses (the reported value) and on one thread."""
     import oracle
     from bit_groupwise_weight_amd.workloads import make_bias, make_weight, make_x
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         threads = max([i.get("num_threads", 1) for i in info] or [1])
+        limit = threadpoolctl.threadpool_limits
     except Exception:
-        threads = 1
-    total_bytes, total_s = 0, 0.0
+        threads, limit = 1, None
+    model, nproc = host_cpu()
+    prepared = []
     for c in cases:
         W = make_weight(c).numpy()
         ref = oracle.quantize(W, c.bits, c.group, c.act)
         x = make_x(c).float().numpy()
         b = make_bias(c)
-        b = None if b is None else b.float().numpy()
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            oracle.linear(x, ref["q"], ref["s"], ref["z"], c.group, b)
-            total_s += time.perf_counter() - t0
-            total_bytes += algo_bytes(c)
+        prepared.append((c, x, ref, None if b is None else b.float().numpy()))
+
+    def run(n):
+        nbytes, secs = 0, 0.0
+        for c, x, ref, b in prepared:
+            for _ in range(n):
+                t0 = time.perf_counter()
+                oracle.linear(x, ref["q"], ref["s"], ref["z"], c.group, b)
+                secs += time.perf_counter() - t0
+                nbytes += algo_bytes(c)
+        return nbytes, secs
+
+    total_bytes, total_s = run(reps)
+    single = None
+    if limit is not None:
+        with limit(limits=1):
+            b1, s1 = run(single_reps)
+        single = {"value": round(b1 / s1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                  "sample": f"the same 7 cases, {single_reps} reps each, one BLAS thread, {s1:.1f} s"}
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"oracle linear (fp64 dequant + matmul) on the 7 decode cases "
                       f"K=N=4096 g64 bits 1..7, {reps} reps each, {total_s:.1f} s total; "
-                      f"quantization excluded"}
+                      f"quantization excluded",
+            "host": {"cpu_model": model, "nproc": nproc, "blas_threads": int(threads)},
+            "single_thread": single}
+
+
+# Workload configurations (bit_groupwise_weight_amd/workloads.py), by key.
+CONFIG_GROUPS = [("single", "single decode", "single_qmv"),
+                 ("llama8b", "Llama-3.1-8B decode", "llama8b_decode"),
+                 ("llama_small", "Llama-3.2-1B/3B decode", "llama_small_decode"),
+                 ("batched", "batched", "batched_qmm"),
+                 ("mixed", "mixed sweep", "mixed_sweep")]
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+
+
+def copies_for(c):
+    return max(2, -(-ROTATE_BYTES // algo_bytes(c)))
+
+
+def case_row(c, us):
+    """Throughput of one case against its bounding roofline: HBM when the
+    case's arithmetic intensity (2MNK flops per algorithmic byte) is below
+    the ridge, MFMA above it."""
+    nb, fl = algo_bytes(c), 2.0 * c.M * c.N * c.K
+    gbps, tfs = nb / (us * 1e-6) / 1e9, fl / (us * 1e-6) / 1e12
+    mfma = fl / nb > RIDGE_FLOP_PER_BYTE
+    return {"case": c.name, "M": c.M, "K": c.K, "N": c.N, "bits": c.bits, "group": c.group,
+            "act": c.act, "bias": c.bias, "us": round(us, 3), "bytes": nb,
+            "GB_s": round(gbps, 1), "TFLOP_s": round(tfs, 2),
+            "bound": "mfma" if mfma else "hbm",
+            "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS if mfma else gbps / HBM_PEAK_GBPS, 4)}
+
+
+def all_configs(dev, stream, reps, only):
+    """Every workload configuration, each case graph-timed over its own
+    rotation of >= 1 GiB of weight copies; plus the single-launch floor (a
+    plain read of the same bytes) at the wide Llama-3.1-8B decode shapes."""
+    from bit_groupwise_weight_amd import workloads
+    rows, summary, wide = [], [], []
+    for key, label, fn in CONFIG_GROUPS:
+        if only and key not in only:
+            continue
+        grows = []
+        for c in getattr(workloads, fn)():
+            p = prepare(c, copies_for(c), dev)
+            torch.cuda.synchronize()
+            n = len(p["sets"])
+            g = capture(lambda i, s: launch(p, i, s), n, stream)
+            us = time_graph(g, max(1, reps // n + 1), n, stream)
+            del g, p
+            torch.cuda.empty_cache()
+            r = case_row(c, us)
+            r["config"] = key
+            grows.append(r)
+            log(f"[{key}] {c.name}: {us:.3f} us  {r['GB_s']} GB/s  {r['TFLOP_s']} TFLOP/s  "
+                f"({r['bound']} frac {r['frac']})")
+            if key == "llama8b" and c.N != c.K and 1024 not in (c.N, c.K):
+                wide.append((c, us))
+        us_all = sorted(r["us"] for r in grows)
+        summary.append({"config": key, "label": label, "cases": len(grows),
+                        "us_min": us_all[0], "us_median": us_all[len(us_all) // 2],
+                        "us_max": us_all[-1],
+                        "frac_min": min(r["frac"] for r in grows),
+                        "frac_median": sorted(r["frac"] for r in grows)[len(grows) // 2],
+                        "frac_max": max(r["frac"] for r in grows)})
+        rows += grows
+    floor_wide = None
+    if wide:
+        reads = plain_read_us([algo_bytes(c) for c, _ in wide], dev, stream, reps)
+        floor_wide = []
+        for (c, us), (r_us, lpt) in zip(wide, reads):
+            nb = algo_bytes(c)
+            floor_wide.append({"case": c.name, "bytes": nb, "qmv_us": round(us, 3),
+                               "stream_read_us": round(r_us, 3), "stream_read_loads_per_thread": lpt,
+                               "stream_read_GB_s": round(nb / (r_us * 1e-6) / 1e9, 1),
+                               "qmv_over_stream_read": round(us / r_us, 3),
+                               "qmv_frac_hbm_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+            log(f"floor {c.name}: plain read {r_us:.3f} us, qmv {us:.3f} us")
+    return {"summary": summary, "cases": rows, "floor_wide": floor_wide,
+            "note": "kernel us = HIP-event time of replays of a graph of back-to-back launches over "
+                    "the case's own weight copies (>= 1 GiB) / launches; bound = mfma when "
+                    "2MNK / algorithmic bytes exceeds the ridge (2.5 PFLOP/s / 8 TB/s), else hbm; "
+                    "floor_wide = plain 16-byte streaming read of the same bytes in one launch"}
 
 
 def main():
@@ -361,9 +512,6 @@ def main():
     qcases, mcases = qmv_cases(), qmm_cases()
     qmv_bytes_all = sum(algo_bytes(c) for c in qcases)
     qmm_bytes_all = sum(algo_bytes(c) for c in mcases)
-
-    def copies_for(c):
-        return max(2, -(-ROTATE_BYTES // algo_bytes(c)))
 
     log("preparing: weight copies per case " +
         ", ".join(str(copies_for(c)) for c in qcases + mcases))
@@ -516,6 +664,11 @@ def main():
                   "launches (rotating weight copies) / launches; steps replay one graph per "
                   "step; qmv_eager_us_per_call = one Python call per launch (host-bound)",
     }
+    if args.all_configs:
+        del qp, mp, step_graphs
+        torch.cuda.empty_cache()
+        only = set(k for k in args.only_configs.split(",") if k)
+        out["all_configs"] = all_configs(dev, stream, args.reps, only)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline(qcases, args.cpu_sample_reps)
