@@ -394,6 +394,10 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   }
   if (sc.tiles_m > 65535 || sc.tiles_n > 0x7fffffff)
     return fail(LOWBIT_ERR_INVALID_ARG, "problem too large for qmm");
+  // the bf16 kernel addresses activations and packed codes with 32-bit
+  // lane offsets from a per-step base
+  if (act == LOWBIT_BF16 && (M * K * 2 > int64_t{0xffffffff} || N * (K * bits / 8) > int64_t{0xffffffff}))
+    return fail(LOWBIT_ERR_UNSUPPORTED, "bf16 qmm: activations and packed codes must each be below 4 GiB");
   lowbit::QmmParams p{};
   p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
   p.M = static_cast<int>(M);

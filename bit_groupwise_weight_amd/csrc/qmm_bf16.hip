@@ -27,7 +27,20 @@
 // 4, wave w runs the ones-MFMA for tile w of each chunk, writes the sums to
 // LDS, and every wave adds z * X one step later, after the barrier that
 // publishes them.
+//
+// Pipeline: three LDS stages, each holding one K step's activation tile,
+// the code runs of every (wave, column tile) and the scales / zeros of every
+// (wave, pass).  All of it arrives by direct global -> LDS loads issued two
+// steps ahead; at the end of a step each wave waits for its own loads of the
+// next step only (an exact count, since every load of the loop is issued by
+// hand) and then meets the others at a barrier without a fence.  Per-lane
+// load offsets are fixed for the whole loop: each step adds one scalar base.
+// The A fragments of the next (chunk, k-sub) slot are read from LDS before
+// the MFMAs of the current one.
 #include "qmm_common.h"
+
+// the direct loads below name M0, which the compiler reserves, as clobbered
+#pragma clang diagnostic ignored "-Winline-asm"
 
 #ifndef LOWBIT_BITS
 #error "compile with -DLOWBIT_BITS=<1..7>"
@@ -75,19 +88,73 @@ __device__ __forceinline__ float4_t mfma_bf16(u32x4_t a, u32x4_t b, float4_t c) 
                                                  __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
 }
 
+// ---- direct global -> LDS loads, issued and counted by hand
+//
+// Every global load of the main loop is a direct load into LDS written in
+// inline assembly: the kernel then knows exactly how many of its loads are
+// in flight, and before each barrier waits (vmcnt) only for the loads of the
+// next step, never for those of the step after it.  (A compiler-placed wait
+// cannot be that precise here: a fence drains every load, and the compiler
+// does not track which stage a direct load writes across the loop.)  Lane l
+// of a 16-byte load writes LDS at M0 + 16 l; of a 4- or 2-byte load, at
+// M0 + 4 l (2 bytes zero-extended).
+
+// global_load_lds_dwordx4 with a scalar base and a 32-bit lane offset
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+               : : "v"(voff), "s"(m0), "s"(sbase) : "memory", "m0");
+}
+// global_load_lds_dwordx4 with a 64-bit lane address
+__device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               : : "v"(vaddr), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, %2"
+               : : "v"(voff), "s"(m0), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_v(const void* vaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               : : "v"(vaddr), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma2_v(const void* vaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off"
+               : : "v"(vaddr), "s"(m0) : "memory", "m0");
+}
+// Wait until at most N of this wave's loads are in flight and its LDS
+// accesses are done, then meet the other waves.  No fence: the memory
+// clobber alone keeps the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void wait_loads_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Code words of a run as direct loads: a 16-byte piece for the first four
+// words when there are four or more, single words for the rest.
+template <int BITS> struct CodePieces {
+  static constexpr int x4 = BITS >= 4 ? 1 : 0;          // one 16-byte piece (words 0..3)
+  static constexpr int singles = BITS - 4 * x4;         // then one word each
+  static constexpr int count = x4 + singles;            // loads per run
+};
+
 template <int BITS, int MTT, int NT, int NP>
 __global__ __launch_bounds__(256, 1) void qmm_bf16_kernel(QmmParams p) {
+  static_assert(NT == 2, "the scale / zero loads pack 2 column tiles x 16 columns x (s, z) into 64 lanes");
   constexpr int WC = 4;
-  constexpr int STAGE = MTT * 16 * 16;        // uint4 per step's activation tile
   constexpr int MC = MTT < 4 ? MTT : 4;       // row tiles per chunk
   constexpr int LPP = 4 / NP;                 // lane groups per pass
-  // two activation stages as two arrays: every access below names its
-  // stage statically (the loop is unrolled by two), so the compiler can see
-  // that reads of one stage never alias the direct loads into the other and
-  // need not wait for those loads before reading
-  __shared__ uint4 stage_a[STAGE];
-  __shared__ uint4 stage_b[STAGE];
-  __shared__ float4_t xsum[2][NP][MTT * 4];   // [step parity][pass][row quad]: X of 4 rows
+  // one pipeline stage: the activation tile, then the code runs of each
+  // (wave, column tile), then the scales / zeros of each (wave, pass)
+  constexpr int XBYTES = MTT * 16 * 16 * 16;
+  constexpr int CBYTES = WC * NT * 256 * BITS;
+  constexpr int SBYTES = WC * NP * 256;
+  constexpr int STAGE = XBYTES + CBYTES + SBYTES;
+  constexpr int NSTAGE = 3;
+  constexpr int XSUM = 2 * NP * MTT * 4 * 16;  // [step parity][pass][row quad] float4
+  constexpr int LOADS = MTT + NT * CodePieces<BITS>::count + NP;   // direct loads per step and wave
+  static_assert(NSTAGE * STAGE + XSUM <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) uint4 smem[(NSTAGE * STAGE + XSUM) / 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
@@ -101,68 +168,88 @@ __global__ __launch_bounds__(256, 1) void qmm_bf16_kernel(QmmParams p) {
   const int s_end = min(ksteps, s_begin + p.ksteps_per_split);
   const int nsteps = s_end - s_begin;
   const int gstep = QMM_BK / NP;              // K per pass (the group size when < 128)
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)));
+  float4_t* xsum = reinterpret_cast<float4_t*>(reinterpret_cast<char*>(smem) + NSTAGE * STAGE);
 
-  int64_t wrow[NT], szrow[NT];
+  // ---- per-lane load offsets (fixed for the whole K loop)
+  // activations: load i of this wave fills rows 4q .. 4q+3 (q = WC i + wave)
+  // of the tile, lane l row 4q + l/16, LDS chunk l%16 <- global chunk
+  // (l%16) ^ swizzle(row)
+  uint32_t xoff[MTT];                         // bytes from the step's first column
+  int xrowc[MTT], xch[MTT];
+#pragma unroll
+  for (int i = 0; i < MTT; ++i) {
+    const int row = 4 * (WC * i + wave) + (lane >> 4);
+    xch[i] = 8 * ((lane & 15) ^ stage_swizzle(row & 15));
+    xrowc[i] = min(m0 + row, p.M - 1);
+    xoff[i] = static_cast<uint32_t>(2 * (static_cast<int64_t>(xrowc[i]) * p.K + xch[i]));
+  }
+  // codes: this lane's run (lane group g) of column n of each column tile
+  uint32_t coff[NT];
+  int ncl[NT];
   uint32_t nok[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int n = n0 + 16 * NT * wave + 16 * nt + fr;
     nok[nt] = 0u - static_cast<uint32_t>(n < p.N);
-    const int nc = min(n, p.N - 1);
-    wrow[nt] = static_cast<int64_t>(nc) * p.row_bytes;
-    szrow[nt] = static_cast<int64_t>(nc) * p.groups;
+    ncl[nt] = min(n, p.N - 1);
+    coff[nt] = static_cast<uint32_t>(static_cast<int64_t>(ncl[nt]) * p.row_bytes + 4 * g * BITS);
   }
-  const uint16_t* sc_bits = static_cast<const uint16_t*>(p.scales);
-  const uint16_t* ze_bits = static_cast<const uint16_t*>(p.zeros);
+  // scales / zeros: lane L loads (L < 32 ? scale : zero) of column
+  // 16 (L/16 % 2) + L%16 of this wave's columns
+  const uint16_t* szp;
+  {
+    const int n = min(n0 + 16 * NT * wave + 16 * ((lane >> 4) & 1) + fr, p.N - 1);
+    szp = static_cast<const uint16_t*>(lane < 32 ? p.scales : p.zeros) + static_cast<int64_t>(n) * p.groups;
+  }
 
-  // codes of one step (this lane's run of each column tile) and the raw
-  // scale / zero of each pass's group, masked to zero past K, past the
-  // block's steps and past N
-  struct Codes {
-    uint32_t w[NT][BITS];
-    uint32_t s[NT][NP], z[NT][NP];
-  };
-  auto load_codes = [&](int u, Codes& c) {
+  // ---- issue the direct loads of step u into stage st (LOADS per wave)
+  auto issue = [&](int u, int st) {
     const int step = s_begin + u;
-    const int st = min(step, s_end - 1);
-    const int kc = min(st * QMM_BK + 32 * g, p.K - 32);
+    const int kb = step * QMM_BK;
+    const uint32_t sb = lds0 + st * STAGE;
+    const bool tail = kb + QMM_BK > p.K;      // block-uniform: only a ragged last step
+    if (!tail) {
+      const char* xb = static_cast<const char*>(p.x) + 2 * static_cast<int64_t>(kb);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      load_run_words<BITS>(p.packed + wrow[nt] + (kc >> 3) * BITS, c.w[nt]);
+      for (int i = 0; i < MTT; ++i) dma16_s(xoff[i], xb, sb + (WC * i + wave) * 1024);
+      const uint8_t* cb = p.packed + static_cast<int64_t>(step) * 16 * BITS;
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        const int kp = st * QMM_BK + pp * gstep;
-        const uint32_t ok = nok[nt] & (0u - static_cast<uint32_t>((step < s_end) & (kp < p.K)));
-        const int64_t gi = szrow[nt] + (min(kp, p.K - 1) >> p.group_shift);
-        c.s[nt][pp] = sc_bits[gi] & ok;
-        c.z[nt][pp] = ze_bits[gi] & ok;
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t cl = sb + XBYTES + (wave * NT + nt) * 256 * BITS;
+        if constexpr (CodePieces<BITS>::x4) dma16_s(coff[nt], cb, cl);
+#pragma unroll
+        for (int j = 0; j < CodePieces<BITS>::singles; ++j) {
+          const int wo = 4 * CodePieces<BITS>::x4 + j;
+          dma4_s(coff[nt], cb + 4 * wo, cl + 256 * wo);
+        }
+      }
+    } else {
+      // ragged last step: clamp every address into its row
+#pragma unroll
+      for (int i = 0; i < MTT; ++i)
+        dma16_v(static_cast<const char*>(p.x) +
+                    2 * (static_cast<int64_t>(xrowc[i]) * p.K + min(kb + xch[i], p.K - 8)),
+                sb + (WC * i + wave) * 1024);
+      const int kc = min(kb + 32 * g, p.K - 32);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t cl = sb + XBYTES + (wave * NT + nt) * 256 * BITS;
+        const uint8_t* src = p.packed + static_cast<int64_t>(ncl[nt]) * p.row_bytes + (kc >> 3) * BITS;
+        if constexpr (CodePieces<BITS>::x4) dma16_v(src, cl);
+#pragma unroll
+        for (int j = 0; j < CodePieces<BITS>::singles; ++j) {
+          const int wo = 4 * CodePieces<BITS>::x4 + j;
+          dma4_v(src + 4 * wo, cl + 256 * wo);
+        }
       }
     }
-  };
-
-  // activation stage (as in the fp16 kernel, one K group)
-  constexpr int RQ = 4 * MTT;
-  constexpr int XL = (RQ + WC - 1) / WC;
-  const uint16_t* xrow[XL];
-  int xchunk[XL];
 #pragma unroll
-  for (int i = 0; i < XL; ++i) {
-    const int q = min(WC * i + wave, RQ - 1);
-    const int row = 4 * q + (lane >> 4);
-    xchunk[i] = 8 * ((lane & 15) ^ stage_swizzle(row & 15));
-    xrow[i] = static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.K;
-  }
-  // straight from global memory into the stage (16 bytes per lane, lane l
-  // of load i of this wave landing at uint4 (WC*i + wave)*64 + l): no
-  // registers hold the next step's activations
-  auto dma_x = [&](int u, uint4* stage) {
-    const int kb = min(s_begin + u, s_end - 1) * QMM_BK;
-#pragma unroll
-    for (int i = 0; i < XL; ++i)
-      if (RQ % WC == 0 || WC * i + wave < RQ)    // wave-uniform
-        __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void*)(xrow[i] + min(kb + xchunk[i], p.K - 8)),
-            (__attribute__((address_space(3))) void*)(stage + (WC * i + wave) * 64), 16, 0, 0);
+    for (int pp = 0; pp < NP; ++pp) {
+      const int kp = min(kb + pp * gstep, p.K - 1);
+      dma2_v(szp + (kp >> p.group_shift), sb + XBYTES + CBYTES + (wave * NP + pp) * 256);
+    }
   };
 
   // lanes of pass pp: lane groups [LPP*pp, LPP*(pp+1))
@@ -189,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void qmm_bf16_kernel(QmmParams p) {
       }
 #pragma unroll
       for (int mt = 0; mt < MTT; ++mt) {
-        const float4_t xv = xsum[parity][pp][4 * mt + g];
+        const float4_t xv = xsum[(parity * NP + pp) * (MTT * 4) + 4 * mt + g];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -198,33 +285,58 @@ __global__ __launch_bounds__(256, 1) void qmm_bf16_kernel(QmmParams p) {
     }
   };
 
-  Codes cc, cn;
-  dma_x(0, stage_a);
-  load_codes(0, cc);
-  __syncthreads();
+  // ---- prologue: steps 0 and 1 in flight, step 0 landed everywhere
+  issue(0, 0);
+  if (nsteps > 1) {
+    issue(1, 1);
+    wait_loads_then_barrier<LOADS>();
+  } else {
+    wait_loads_then_barrier<0>();
+  }
 
-  // one K step: reads stage `cur`, loads the next step into `nxt`
-  auto step = [&](const int u, const uint4* cur, uint4* nxt, const int par) {
-    // next step's loads, in flight during this step (the barrier at its
-    // end waits for them: stage u+1 is then complete)
-    dma_x(u + 1, nxt);
-    load_codes(u + 1, cn);
+  int st = 0;                                  // stage of step u
+  for (int u = 0; u < nsteps; ++u) {
+    const bool more = u + 2 < nsteps;          // block-uniform
+    if (more) issue(u + 2, st == 0 ? 2 : st - 1);
+    const int par = u & 1;
+    const char* sbase = reinterpret_cast<const char*>(smem) + st * STAGE;
+    const uint4* cur = reinterpret_cast<const uint4*>(sbase);
 
+    // scales and zeros of this lane's column in each column tile and pass
     float sf[NT][NP], zf[NT][NP];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    {
+      const uint32_t* szl = reinterpret_cast<const uint32_t*>(sbase + XBYTES + CBYTES) + wave * NP * 64;
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) {
-        sf[nt][pp] = bf16_bits_to_float(cc.s[nt][pp]);
-        zf[nt][pp] = bf16_bits_to_float(cc.z[nt][pp]);
+        const int kp = (s_begin + u) * QMM_BK + pp * gstep;
+        const uint32_t kok = 0u - static_cast<uint32_t>(kp < p.K);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t ok = nok[nt] & kok;
+          sf[nt][pp] = bf16_bits_to_float(szl[pp * 64 + 16 * nt + fr] & ok);
+          zf[nt][pp] = bf16_bits_to_float(szl[pp * 64 + 32 + 16 * nt + fr] & ok);
+        }
       }
+    }
+    // this lane's code words and the B operands of the four k-subs
     u32x4_t bq[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      bq[nt][0] = code_operand<BITS, 0>(cc.w[nt]);
-      bq[nt][1] = code_operand<BITS, 1>(cc.w[nt]);
-      bq[nt][2] = code_operand<BITS, 2>(cc.w[nt]);
-      bq[nt][3] = code_operand<BITS, 3>(cc.w[nt]);
+      const char* cl = sbase + XBYTES + (wave * NT + nt) * 256 * BITS;
+      uint32_t w[BITS];
+      if constexpr (CodePieces<BITS>::x4) {
+        const uint4 v = reinterpret_cast<const uint4*>(cl)[lane];
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < CodePieces<BITS>::singles; ++j) {
+        const int wo = 4 * CodePieces<BITS>::x4 + j;
+        w[wo] = reinterpret_cast<const uint32_t*>(cl + 256 * wo)[lane];
+      }
+      bq[nt][0] = code_operand<BITS, 0>(w);
+      bq[nt][1] = code_operand<BITS, 1>(w);
+      bq[nt][2] = code_operand<BITS, 2>(w);
+      bq[nt][3] = code_operand<BITS, 3>(w);
     }
     if (u > 0) add_offset(par ^ 1, zprev);
     // row tiles in chunks of MC (the group sums P of one chunk at a time,
@@ -242,56 +354,63 @@ __global__ __launch_bounds__(256, 1) void qmm_bf16_kernel(QmmParams p) {
 #pragma unroll
         for (int q = 1; q < NP; ++q) sp[nt] = pp == q ? sf[nt][q] : sp[nt];
       }
+      // slots t = 4 c + ks over the chunks c and k-subs ks; the A fragments
+      // of slot t+1 are read before the MFMAs of slot t (two buffers), so
+      // the MFMAs wait on reads issued one slot earlier
+      constexpr int T = (MTT / MC) * 4;
+      const bool xw = MC == WC || wave < MC;    // wave-uniform: this wave computes X of a tile
+      u32x4_t fa[2][MC + 1];
+      auto read_slot = [&](int t, u32x4_t (&f)[MC + 1]) {
+        const int c = t >> 2, ks = t & 3;
+        const int chunk = (4 * g + ks) ^ stage_swizzle(fr);
 #pragma unroll
-      for (int c = 0; c < MTT / MC; ++c) {
-        float4_t P[MC][NT];
-        float4_t Xa;
-        const bool xw = MC == WC || wave < MC;    // wave-uniform
-        const int xmt = MC * c + (xw ? wave : 0);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          u32x4_t af[MC];
-#pragma unroll
-          for (int j = 0; j < MC; ++j)
-            af[j] = reinterpret_cast<const u32x4_t*>(cur)[(16 * (MC * c + j) + fr) * 16 +
-                                                            ((4 * g + ks) ^ stage_swizzle(fr))];
-#pragma unroll
-          for (int j = 0; j < MC; ++j)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              P[j][nt] = mfma_bf16(af[j], NP == 1 ? bq[nt][ks] : (bq[nt][ks] & pm),
-                                   ks == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : P[j][nt]);
-          if (xw) {
-            const u32x4_t xa = reinterpret_cast<const u32x4_t*>(cur)[(16 * xmt + fr) * 16 +
-                                                                       ((4 * g + ks) ^ stage_swizzle(fr))];
-            Xa = mfma_bf16(xa, NP == 1 ? ones : (ones & pm), ks == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : Xa);
-          }
-        }
+        for (int j = 0; j < MC; ++j)
+          f[j] = reinterpret_cast<const u32x4_t*>(cur)[(16 * (MC * c + j) + fr) * 16 + chunk];
+        if (xw)
+          f[MC] = reinterpret_cast<const u32x4_t*>(cur)[(16 * (MC * c + wave) + fr) * 16 + chunk];
+      };
+      read_slot(0, fa[0]);
+      float4_t P[MC][NT];
+      float4_t Xa;
+      static_for<T>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int c = t / 4, ks = t % 4;
+        if constexpr (t + 1 < T) read_slot(t + 1, fa[(t + 1) % 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4_t(&f)[MC + 1] = fa[t % 2];
 #pragma unroll
         for (int j = 0; j < MC; ++j)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
+            P[j][nt] = mfma_bf16(f[j], NP == 1 ? bq[nt][ks] : (bq[nt][ks] & pm),
+                                 ks == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : P[j][nt]);
+        if (xw) Xa = mfma_bf16(f[MC], NP == 1 ? ones : (ones & pm), ks == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : Xa);
+        if constexpr (ks == 3) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              tot[MC * c + j][nt][i] = __builtin_fmaf(sp[nt], P[j][nt][i], tot[MC * c + j][nt][i]);
-        // every column of the ones product holds the row sums: the lanes of
-        // column 0 publish rows 4g .. 4g+3 of the tile
-        if (xw && fr == 0) xsum[par][pp][4 * xmt + g] = Xa;
-      }
+          for (int j = 0; j < MC; ++j)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                tot[MC * c + j][nt][i] = __builtin_fmaf(sp[nt], P[j][nt][i], tot[MC * c + j][nt][i]);
+          // every column of the ones product holds the row sums: the lanes of
+          // column 0 publish rows 4g .. 4g+3 of the tile
+          if (xw && fr == 0) xsum[(par * NP + pp) * (MTT * 4) + 4 * (MC * c + wave) + g] = Xa;
+        }
+      });
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) zprev[nt][pp] = zf[nt][pp];
-    __syncthreads();   // stage u+1 and the sums of step u are published; stage u is read
-    cc = cn;
-  };
-  int u = 0;
-  for (; u + 2 <= nsteps; u += 2) {
-    step(u, stage_a, stage_b, 0);
-    step(u + 1, stage_b, stage_a, 1);
+    // step u+1 (issued one step ago) has landed in every wave's part of its
+    // stage, the sums of step u are published, and stage u is read
+    if (more)
+      wait_loads_then_barrier<LOADS>();
+    else
+      wait_loads_then_barrier<0>();
+    st = st == NSTAGE - 1 ? 0 : st + 1;
   }
-  if (u < nsteps) step(u, stage_a, stage_b, 0);
   add_offset((nsteps - 1) & 1, zprev);
 
   // ---- epilogue (lane holds D[4g + r][fr] of each 16x16 tile)
@@ -311,7 +430,8 @@ __global__ __launch_bounds__(256, 1) void qmm_bf16_kernel(QmmParams p) {
     }
     return;
   }
-  // split-K partial records, laid out as the fp16 kernel's (one K group)
+  // split-K partial records, laid out as the fp16 kernel's (one K group);
+  // the reduce kernel adds the planes in split order
   const int64_t tile = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
   const int64_t plane_recs = static_cast<int64_t>(gridDim.x) * gridDim.y * (WC * MTT * NT * 64);
   float4_t* part = reinterpret_cast<float4_t*>(p.partials) + (tile * WC + wave) * (MTT * NT * 64) + lane;
