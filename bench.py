@@ -171,15 +171,30 @@ def time_graph(g, replays, per_replay, stream):
     return e0.elapsed_time(e1) * 1e3 / (replays * per_replay)
 
 
-def time_eager(p, reps, stream):
-    """Microseconds per call when launched one by one from Python (host-bound)."""
+def time_eager(p, reps, stream, prepared=True):
+    """Microseconds per call when launched one by one from Python (host-bound):
+    through a PreparedLinear per weight copy (weights validated once, as the
+    module's eager forward does), or through lowbit_linear (every tensor
+    validated on every call)."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    c = p["case"]
+    if prepared:
+        calls = [lb.PreparedLinear(pk, s, z, p["bias"], c.bits, c.group) for (pk, s, z) in p["sets"]]
+        n = len(calls)
+
+        def one(i):
+            calls[i % n](p["x"], y=p["ys"][i % 2], stream=stream)
+    else:
+        def one(i):
+            launch(p, i, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     for i in range(3):
-        launch(p, i, stream)
+        one(i)
+    torch.cuda.synchronize()
     e0.record(stream)
     for i in range(reps):
-        launch(p, i, stream)
+        one(i)
     e1.record(stream)
     e1.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
@@ -559,6 +574,8 @@ def main():
     qmv_us = [kernel_us(p) for p in qp]
     qmm_us = [kernel_us(p) for p in mp]
     eager_us = None if args.no_eager else [time_eager(p, args.reps, stream) for p in qp]
+    eager_generic_us = None if args.no_eager else [time_eager(p, args.reps, stream, prepared=False)
+                                                   for p in qp]
     per_bit = []
     for c, us in zip(qcases, qmv_us):
         gbps = algo_bytes(c) / (us * 1e-6) / 1e9
@@ -659,10 +676,14 @@ def main():
         },
         "qmm": qmm,
         "qmv_eager_us_per_call": None if eager_us is None else [round(u, 3) for u in eager_us],
+        "qmv_eager_us_per_call_generic": None if eager_generic_us is None
+        else [round(u, 3) for u in eager_generic_us],
         "decode_layer": decode_layer,
         "timing": "per-kernel us = HIP-event time of replays of a HIP graph of back-to-back "
                   "launches (rotating weight copies) / launches; steps replay one graph per "
-                  "step; qmv_eager_us_per_call = one Python call per launch (host-bound)",
+                  "step; qmv_eager_us_per_call = one Python call per launch through a "
+                  "PreparedLinear (weights validated once, output preallocated; host-bound); "
+                  "_generic = through lowbit_linear, every tensor validated per call",
     }
     if args.all_configs:
         del qp, mp, step_graphs

@@ -313,6 +313,92 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
     return y
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+class PreparedLinear:
+    """One layer's weights bound to lowbit_linear once, for eager calls.
+
+    The weight tensors (packed, scales, zeros, bias) are validated when the
+    object is made and their device pointers kept (with references to the
+    tensors); a call then checks only x and y, takes the current stream's raw
+    handle and the workspace cached for (M, stream), and makes the one C call.
+    The result is that of lowbit_linear with the same arguments.  Rebuild the
+    object if the weight tensors are replaced (in-place updates keep it valid).
+    """
+
+    __slots__ = ("N", "K", "bits", "group", "dtype", "act", "device", "dev_index", "_ptrs",
+                 "_keep", "_fn", "_ws", "_const", "_one_device")
+
+    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                 bias: Optional[torch.Tensor], bits: int, group: int):
+        lib = load()
+        _expect(scales.dim() == 2, "scales must be 2-D [N, K/group]")
+        dt = scales.dtype
+        _expect(dt in _DTYPE_ENUM, f"scales dtype {dt} is not float32, float16 or bfloat16")
+        N, G = scales.shape
+        K = G * group
+        _check_weight_tensors(packed, scales, zeros, N, K, bits, group, dt)
+        if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or bias.dtype != dt):
+            raise ValueError(f"bias must be [{N}] of {dt}")
+        _require_cuda(packed, scales, zeros, bias)
+        self.N, self.K, self.bits, self.group = N, K, bits, group
+        self.dtype, self.act = dt, _DTYPE_ENUM[dt]
+        self.device = packed.device
+        self.dev_index = packed.get_device()
+        self._one_device = torch.cuda.device_count() == 1   # then no device switch is ever needed
+        self._ptrs = (packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), _ptr(bias))
+        self._keep = (packed, scales, zeros, bias)
+        # the same entry point without argument types: every argument is
+        # passed as a ready ctypes value (the ones fixed for this layer are
+        # made here), which skips the per-argument conversion of a call
+        self._fn = type(lib.lowbit_linear)(("lowbit_linear", lib))
+        self._fn.restype = ctypes.c_int
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        self._const = (ci(self.act), vp(self._ptrs[0]), vp(self._ptrs[1]), vp(self._ptrs[2]),
+                       vp(self._ptrs[3]), ci(bits), ci(group), ctypes.c_int64(N), ctypes.c_int64(K))
+        self._ws = {}
+
+    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """y[M, N] = x[M, K] . dequant(W)^T (+ bias) for this layer."""
+        if (x.dtype is not self.dtype or x.dim() != 2 or x.shape[1] != self.K
+                or x.get_device() != self.dev_index or not x.is_contiguous()):
+            raise ValueError(f"x must be a contiguous [M, {self.K}] {self.dtype} tensor on {self.device}")
+        M = x.shape[0]
+        N = self.N
+        if y is None:
+            y = torch.empty((M, N), dtype=self.dtype, device=self.device)
+        elif (y.dtype is not self.dtype or y.dim() != 2 or y.shape[0] != M or y.shape[1] != N
+              or y.get_device() != self.dev_index or not y.is_contiguous()):
+            raise ValueError(f"y must be a contiguous [{M}, {N}] {self.dtype} tensor on {self.device}")
+        if stream is not None:
+            s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        elif _raw_stream is not None:
+            s = _raw_stream(self.dev_index)
+        else:
+            s = torch.cuda.current_stream(self.device).cuda_stream
+        key = (M, s)
+        tail = self._ws.get(key)
+        if tail is None:
+            need = load().lowbit_linear_workspace_bytes(self.bits, self.group, M, N, self.K, self.act)
+            buf = cached_workspace(self.device, s, need) if M > 0 else None
+            ws_ptr, ws_bytes = (None, 0) if buf is None else (buf.data_ptr(), buf.numel())
+            tail = (ctypes.c_int64(M), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(s))
+            self._ws[key] = tail
+        act, pk, sp, zp, bp, bits, group, n, k = self._const
+        m, wp, wb, sh = tail
+        args = (ctypes.c_void_p(x.data_ptr()), act, pk, sp, zp, bp, ctypes.c_void_p(y.data_ptr()),
+                bits, group, m, n, k, wp, wb, sh)
+        if self._one_device or torch.cuda.current_device() == self.dev_index:
+            st = self._fn(*args)
+        else:
+            with torch.cuda.device(self.device):
+                st = self._fn(*args)
+        if st != LOWBIT_OK:
+            _check(st, "lowbit_linear")
+        return y
+
+
 def lowbit_linear_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                           zeros: torch.Tensor, bias: Optional[torch.Tensor], bits: int, group: int,
                           y: torch.Tensor, stream=None) -> torch.Tensor:

@@ -129,6 +129,7 @@ class LowbitLinear(torch.nn.Module):
             raise ValueError(f"in_features={in_features} is not a multiple of group_size={group_size}")
         self.in_features, self.out_features = in_features, out_features
         self.bits, self.group_size, self.dtype = bits, group_size, dtype
+        self._call = None            # prepared eager call (made on first use)
         G = in_features // group_size
         self.register_buffer("packed", torch.zeros((out_features, in_features * bits // 8),
                                                    dtype=torch.uint8, device=device))
@@ -166,8 +167,25 @@ class LowbitLinear(torch.nn.Module):
         return m.set_weight(lin.weight, lin.bias)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return torch.ops.lowbit.linear(x, self.packed, self.scales, self.zeros, self.bias,
-                                       self.bits, self.group_size)
+        # Traced (torch.compile), autograd and non-GPU (e.g. meta) calls go
+        # through the registered op; plain eager GPU calls take the prepared
+        # call, which validated the weights once (buffers replaced by .to()
+        # and the like make a new one).
+        if (not x.is_cuda or torch.compiler.is_compiling()
+                or (x.requires_grad and torch.is_grad_enabled())):
+            return torch.ops.lowbit.linear(x, self.packed, self.scales, self.zeros, self.bias,
+                                           self.bits, self.group_size)
+        b = self._buffers
+        call = self._call
+        if (call is None or call._keep[0] is not b["packed"] or call._keep[1] is not b["scales"]
+                or call._keep[2] is not b["zeros"] or call._keep[3] is not b.get("bias")):
+            call = _lb.PreparedLinear(b["packed"], b["scales"], b["zeros"], b.get("bias"),
+                                      self.bits, self.group_size)
+            self._call = call
+        if x.dim() == 2:
+            return call(x.contiguous())
+        y = call(x.reshape(-1, self.in_features).contiguous())
+        return y.reshape(*x.shape[:-1], self.out_features)
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, bits={self.bits}, "

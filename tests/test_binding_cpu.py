@@ -102,3 +102,15 @@ def test_quantize_refuses_bad_outputs_and_input():
         lb.lowbit_quantize_pack(w.double(), BITS, GROUP, torch.float16)
     with pytest.raises(ValueError, match="GPU memory"):
         lb.lowbit_quantize_pack(w, BITS, GROUP, torch.float16, out=(packed, scales, zeros, None))
+
+
+def test_prepared_linear_checks_weights_once_at_construction():
+    packed, scales, zeros = weights()
+    with pytest.raises(ValueError, match="packed holds"):
+        lb.PreparedLinear(packed[:-1], scales, zeros, None, BITS, GROUP)
+    with pytest.raises(ValueError, match="bias must be"):
+        lb.PreparedLinear(packed, scales, zeros, torch.zeros(N + 1, dtype=torch.float16), BITS, GROUP)
+    with pytest.raises(ValueError, match="zeros must be"):
+        lb.PreparedLinear(packed, scales, zeros.to(torch.bfloat16), None, BITS, GROUP)
+    with pytest.raises(ValueError, match="GPU memory"):
+        lb.PreparedLinear(packed, scales, zeros, None, BITS, GROUP)

@@ -80,3 +80,45 @@ def test_quantize_linears_mlp_matches_oracle():
     y = model[2](torch.relu(h))
     y_ref, A2 = oracle_forward(W2, None, torch.relu(h).cpu(), 6, 64, "f16")
     check_close(y, y_ref, A2, "layer 2")
+
+
+@pytest.mark.parametrize("M,act,bits,group,bias", [
+    (1, "f16", 4, 64, True), (3, "bf16", 7, 32, False), (1, "f32", 2, 128, True),
+    (40, "bf16", 4, 128, True), (96, "f16", 3, 256, False)])
+def test_prepared_call_matches_lowbit_linear(M, act, bits, group, bias):
+    """The prepared eager call is lowbit_linear with the weights bound once:
+    the same output bit for bit (decode and MFMA paths, with and without a K
+    split), with a preallocated y and an explicit stream too."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    case, W, b = module_case(bits, group, act, bias, seed=M + bits, N=200, K=1024)
+    dt = TORCH_ACT[act]
+    packed, s, z = lnn.quantize_pack(W.to(DEV), bits, group, dt)
+    bd = None if b is None else b.to(DEV)
+    x = torch.randn((M, case.K), generator=torch.Generator().manual_seed(M)).to(dt).to(DEV)
+    y_ref = lb.lowbit_linear(x, packed, s, z, bd, bits, group)
+    call = lb.PreparedLinear(packed, s, z, bd, bits, group)
+    y1 = call(x)
+    y2 = torch.full_like(y_ref, float("nan"))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    call(x, y=y2, stream=stream)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y_ref) and torch.equal(y2, y_ref)
+    with pytest.raises(ValueError, match="x must be"):
+        call(x[:, :-32].contiguous())
+
+
+def test_module_rebinds_replaced_buffers():
+    """Buffers replaced after the first call (as .to() or assignment does) are
+    the ones the next eager call reads."""
+    case, W, b = module_case(4, 64, "f16", True, seed=9, N=64, K=256)
+    m = lnn.LowbitLinear(case.K, case.N, 4, 64, bias=True, dtype=torch.float16, device=DEV)
+    m.set_weight(W.to(DEV), b.to(DEV))
+    x = torch.randn((2, case.K), generator=torch.Generator().manual_seed(3)).half().to(DEV)
+    y0 = m(x)
+    m.scales = m.scales.clone()
+    m.zeros = torch.zeros_like(m.zeros)
+    y1 = m(x)
+    op = torch.ops.lowbit.linear(x, m.packed, m.scales, m.zeros, m.bias, 4, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, op) and not torch.equal(y0, y1)
