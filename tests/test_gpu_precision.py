@@ -139,3 +139,23 @@ def test_correlated_weight_rounding(M, act):
     q = np.ones((N, K), np.uint8)
     x = np.ones((M, K), np.float32)
     run_paths(x, q, s, z, None, bits, group, act, f"correlated-rounding M={M} {act}")
+
+
+@pytest.mark.parametrize("bits,group", [(1, 64), (4, 32), (7, 128)])
+@pytest.mark.parametrize("M", [1, 3, 24])
+def test_fp16_near_max_activations(bits, group, M):
+    """fp16 activations near +-6e4 (close to the fp16 maximum) in a few
+    groups, ordinary ones elsewhere, on small weights so that y stays in
+    range: the products x*q and the group sums are far larger than anywhere
+    else, and every path must keep them exact enough."""
+    rng = np.random.default_rng(bits * 31 + M + group)
+    N, K = 96, 2048
+    W = (rng.standard_normal((N, K)) * 1e-4).astype(np.float32)
+    ref = oracle.quantize(W, bits, group, "f16")
+    x = rng.standard_normal((M, K))
+    for gi in rng.choice(K // group, size=3, replace=False):
+        sign = np.where(rng.random((M, group)) < 0.5, -1.0, 1.0)
+        x[:, gi * group:(gi + 1) * group] = sign * rng.uniform(3e4, 6e4, size=(M, group))
+    x = act_round(x, "f16")
+    run_paths(x, ref["q"], ref["s"], ref["z"], None, bits, group, "f16",
+              f"near-max x M={M} b={bits} g={group} f16")
