@@ -61,8 +61,9 @@ typedef enum lowbit_status {
   LOWBIT_OK = 0,
   LOWBIT_ERR_INVALID_ARG = 1,  /* bits/group/shape out of range, NULL pointer      */
   LOWBIT_ERR_UNSUPPORTED = 2,  /* a dtype or path combination that is not built     */
-  LOWBIT_ERR_MISALIGNED = 3,   /* packed not 16-byte aligned, or an array not
-                                  aligned to its element size                       */
+  LOWBIT_ERR_MISALIGNED = 3,   /* packed, x (linear) or w (quantize) not 16-byte
+                                  aligned, or another array not aligned to its
+                                  element size                                      */
   LOWBIT_ERR_NONFINITE = 4,    /* quantize: the weight holds a NaN or an infinity   */
   LOWBIT_ERR_RANGE = 5,        /* quantize: a scale or zero overflows its dtype     */
   LOWBIT_ERR_WORKSPACE = 6,    /* workspace pointer/size inconsistent               */
@@ -130,12 +131,16 @@ size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, 
 /* y = x . dequant(packed, scales, zeros)^T (+ bias), enqueued on `stream`
  * (asynchronous: the call returns once the kernels are launched).
  *
- *   x        device, M x K row-major, act_dtype.
+ *   x        device, M x K row-major, act_dtype, 16-byte aligned (the
+ *            kernels read activations in 16-byte pieces).
  *   packed, scales, zeros   as written by lowbit_quantize_pack with
- *            sz_dtype == act_dtype (or built by the caller in that format).
- *   bias     device, N elements of act_dtype, or NULL for no bias.
- *   y        device, M x N row-major, act_dtype.  Overwritten; must not alias
- *            any input.
+ *            sz_dtype == act_dtype (or built by the caller in that format);
+ *            packed 16-byte aligned, scales and zeros aligned to their
+ *            element size.
+ *   bias     device, N elements of act_dtype, or NULL for no bias; aligned to
+ *            its element size.
+ *   y        device, M x N row-major, act_dtype, aligned to its element size.
+ *            Overwritten; must not alias any input.
  *   M >= 0 (M == 0 is a no-op that returns LOWBIT_OK; x and y may then be
  *   NULL), N > 0, K > 0,
  *   K % group == 0.
@@ -146,8 +151,13 @@ size_t lowbit_linear_workspace_bytes(int bits, int group, int64_t M, int64_t N, 
  *            workspace.
  *
  * Products accumulate in fp32; the bias is added in fp32 and the result is
- * rounded to act_dtype to nearest even.  Identical inputs give bitwise
- * identical outputs (no floating-point atomics). */
+ * rounded to act_dtype to nearest even.  Determinism: two calls with the
+ * same inputs, on the same device model, with the same workspace size (the
+ * same K split) and the same schedule overrides (lowbit_tuning.h) give
+ * bitwise identical outputs -- no floating-point atomics, and the K split's
+ * partial sums are added in a fixed order.  Another workspace size, path or
+ * override may choose another schedule, whose results differ in rounding
+ * (each accumulated and rounded as stated above). */
 lowbit_status lowbit_linear(const void* x, lowbit_dtype act_dtype, const uint8_t* packed,
                             const void* scales, const void* zeros, const void* bias, void* y,
                             int bits, int group, int64_t M, int64_t N, int64_t K,
