@@ -17,7 +17,9 @@
 //     weights are still in flight;
 //   * codes reach the dot products as exact values: fp16 codes by OR-ing
 //     exponent fields (see qmv_plan.h), which gives 2^(10-o) + q, and one
-//     packed fp16 subtract of 2^(10-o) per pair, then v_dot2_f32_f16; bf16
+//     packed fp16 subtract of 2^(10-o) per pair, then v_dot2_f32_f16 (at 2
+//     and 4 bits as fp16 subnormals q * 2^(o-24), one accumulator per bit
+//     offset, without the subtract); bf16
 //     codes through the fp8 conversion (a code below 16 in a byte is the
 //     e4m3 value q * 2^-9) or, above 4 bits, through fp32; fp32 converts
 //     each code.  Only the products x*q enter the fp32 sums, so their
@@ -123,6 +125,58 @@ __device__ __forceinline__ float f16_dot_slots(const uint32_t* w, const uint32_t
   }
 }
 
+// Widths that divide 16 put the two codes of every slot at the same bit
+// offset o of their halves; at 2 and 4 bits (five and two offsets) the form
+// below is the cheaper one.  There the exponent field stays
+// zero: each half is the fp16 subnormal q * 2^(o-24), exact, and v_dot2
+// keeps subnormal inputs (fp16 denormals are on), so one AND and one dot2
+// per pair suffice.  Products of one offset share an fp32 accumulator;
+// the accumulators are combined with exact power-of-two steps
+// (sum x*q = sum_o acc_o * 2^(24-o)), so the rounding stays relative to
+// sum |x*q| as in the general form.
+template <int BITS> struct F16SubPlan {
+  static constexpr bool on = BITS == 2 || BITS == 4;   // (1 bit: ten offsets, no gain)
+  static constexpr int noff = F16Plan<BITS>::span / BITS;   // offsets 0, b, 2b, ...
+};
+
+template <int BITS, int I = 0>
+__device__ __forceinline__ void f16_sub_slots(const uint32_t* w, const uint32_t* xs,
+                                              float (&acc)[F16SubPlan<BITS>::noff]) {
+  if constexpr (I < F16Plan<BITS>::n) {
+    constexpr PairSlot s = F16Plan<BITS>::table.s[I];
+    static_assert(s.klo < 0 || s.khi < 0 || s.olo == s.ohi, "paired codes share their offset");
+    uint32_t win;
+    if constexpr (s.shift == 0) {
+      win = w[s.word];
+    } else if constexpr (s.word + 1 < BITS) {
+      win = __builtin_amdgcn_alignbit(w[s.word + 1], w[s.word], s.shift);
+    } else {
+      win = w[s.word] >> s.shift;
+    }
+    constexpr uint32_t m = (1u << BITS) - 1u;
+    constexpr uint32_t mask = (s.klo >= 0 ? (m << s.olo) : 0u) |
+                              (s.khi >= 0 ? (m << (16 + s.ohi)) : 0u);
+    constexpr int o = s.klo >= 0 ? s.olo : s.ohi;
+    static_assert(o % BITS == 0 && o / BITS < F16SubPlan<BITS>::noff, "offset on the code grid");
+    acc[o / BITS] = dot2<ACT_F16>(xs[I], win & mask, acc[o / BITS]);
+    f16_sub_slots<BITS, I + 1>(w, xs, acc);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float f16_sub_dot(const uint32_t* w, const uint32_t* xs) {
+  constexpr int N = F16SubPlan<BITS>::noff;
+  float acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+  f16_sub_slots<BITS>(w, xs, acc);
+  // sum_i acc_i * 2^(24 - i*b) = 2^24 * (acc_0 + 2^-b * (acc_1 + 2^-b * (...)))
+  float t = acc[N - 1];
+#pragma unroll
+  for (int i = N - 2; i >= 0; --i) t = __builtin_fmaf(t, 1.0f / static_cast<float>(1u << BITS), acc[i]);
+  return t * 16777216.0f;   // 2^24
+}
+
 // Codes 2I and 2I+1 of a run as two exact bf16 values (low half: code 2I).
 // Up to 4 bits, a code q in a byte is the OCP fp8 e4m3 value q * 2^-9 (a
 // subnormal below 8, then the first binade with step 2^-9), so one scaled
@@ -164,7 +218,8 @@ __device__ __forceinline__ float f32_dot(const uint32_t* w, const uint32_t* xs, 
 template <int ACT, int BITS>
 __device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) {
   if constexpr (ACT == ACT_F16) {
-    return f16_dot_slots<BITS>(w, xs, 0.0f);
+    if constexpr (F16SubPlan<BITS>::on) return f16_sub_dot<BITS>(w, xs);
+    else return f16_dot_slots<BITS>(w, xs, 0.0f);
   } else if constexpr (ACT == ACT_BF16) {
     return bf16_dot_pairs<BITS>(w, xs, 0.0f);
   } else {

@@ -7,9 +7,10 @@
 // 32-bit window is turned into the fp16 value 2^(10-o) + q, exactly, by OR-ing
 // the fp16 exponent field (25 - o) above it: the half then reads
 // 2^(10-o) * (1 + q*2^o/1024).  One AND-OR therefore converts two codes (one
-// per half) at once, and one dot2 accumulates x_lo*(2^(10-olo)+q_lo) +
-// x_hi*(2^(10-ohi)+q_hi).  The constant part sum_k x_k*2^(10-o_k) of a run is
-// computed once per activation run and subtracted.
+// per half) at once; one packed subtract of the two constants leaves the
+// codes exactly, and one dot2 accumulates x_lo*q_lo + x_hi*q_hi.  (Where both
+// codes of a pair sit at one offset -- widths dividing 16 -- the decode kernel
+// may instead leave the exponent field zero and read the halves as subnormals.)
 //
 // Windows: word d shifted right by t*span bits (a funnel shift across words d
 // and d+1).  A code whose start lies rel bits into word d (rel < 32) goes to
