@@ -119,6 +119,8 @@ struct QmmLaunch {
   int waves;              // column waves per block: 4, or 8 (bits <= qmm_max_bits_8waves)
   int kgroups;            // K groups per block: 1, or 2 with 4 column waves
                           // (bits <= qmm_max_bits_kgroups); waves*kgroups waves in all
+  int rgroups;            // bf16 kernel: row groups per block, 1 or 2 (each a set of
+                          // `waves` column waves over its share of the row tiles)
 };
 hipError_t launch_qmm_b1(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b2(const QmmParams&, const QmmLaunch&, int act, hipStream_t);

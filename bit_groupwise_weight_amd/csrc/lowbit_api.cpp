@@ -285,7 +285,7 @@ const QmmLauncher kQmm[8] = {nullptr,
 // Schedule of the MFMA kernel: block tile (16*mtt) x (16*nt*waves), K steps
 // of 128, and a K split that fills the CUs with one block each.
 struct QmmSchedule {
-  int mtt, nt, waves, kgroups;
+  int mtt, nt, waves, kgroups, rgroups;
   int64_t tiles_n, tiles_m, ksteps;
   int splits, ksteps_per_split;
   size_t partial_bytes;   // fp32 partial planes (split-K)
@@ -336,14 +336,23 @@ constexpr int kQmmKGroupsMinSteps = 8;
 
 QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
+  sc.rgroups = 1;
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   const int mtt_env = tuning(LOWBIT_TUNE_QMM_MTT, 0);
   if (mtt_env == 1 || mtt_env == 2 || mtt_env == 4 || mtt_env == 8) sc.mtt = std::min(sc.mtt, mtt_env);
   sc.nt = 2;
   if (act == LOWBIT_BF16) {
-    // bf16: the code-operand kernel, 4 column waves of two column tiles
+    // bf16: the code-operand kernel, 4 column waves of two column tiles;
+    // 128-row tiles split between two row groups of 4 waves (two waves per
+    // SIMD; 64-row tiles only when asked)
     sc.waves = 4;
     sc.kgroups = 1;
+    const int rg_env = tuning(LOWBIT_TUNE_QMM_RGROUPS, 0);
+    sc.rgroups = ((sc.mtt == 8 && rg_env != 1) || (sc.mtt == 4 && rg_env == 2)) ? 2 : 1;
+    if (tuning(LOWBIT_TUNE_QMM_NT, 0) == 1) {
+      sc.nt = 1;
+      sc.rgroups = 1;
+    }
     qmm_split(sc, M, N, K);
     return sc;
   }
@@ -415,6 +424,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   l.nt = sc.nt;
   l.waves = sc.waves;
   l.kgroups = sc.kgroups;
+  l.rgroups = sc.rgroups;
   l.grid = dim3(static_cast<unsigned>(sc.tiles_n), static_cast<unsigned>(sc.tiles_m),
                 static_cast<unsigned>(sc.splits));
   hipError_t e = kQmm[bits](p, l, act_kind(act), stream);

@@ -30,7 +30,8 @@ typedef enum lowbit_tuning_key {
   LOWBIT_TUNE_QMM_KGROUPS = 4,  /* fp16 MFMA kernel: 1 or 2 K groups                */
   LOWBIT_TUNE_QMM_NT = 5,       /* fp16 MFMA kernel: 1 or 2 column tiles per wave   */
   LOWBIT_TUNE_QMM_WAVES = 6,    /* fp16 MFMA kernel, one K group: 4 or 8 waves      */
-  LOWBIT_TUNE_COUNT = 7
+  LOWBIT_TUNE_QMM_RGROUPS = 7,  /* bf16 MFMA kernel: 1 or 2 row groups of 4 waves   */
+  LOWBIT_TUNE_COUNT = 8
 } lowbit_tuning_key;
 
 /* Set (value > 0) or clear (value == 0) one override.  LOWBIT_ERR_INVALID_ARG

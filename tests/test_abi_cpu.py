@@ -140,7 +140,8 @@ def test_quantize_validation(lowbit_lib, args, status):
 
 
 def test_tuning_validation(lowbit_lib):
-    assert lowbit_lib.lowbit_set_tuning(7, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(8, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(7, 2) == OK and lowbit_lib.lowbit_set_tuning(7, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(-1, 1) == INVALID
     assert lowbit_lib.lowbit_set_tuning(0, -2) == INVALID
     assert lowbit_lib.lowbit_set_tuning(3, 0) == OK

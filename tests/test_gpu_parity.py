@@ -240,6 +240,21 @@ def test_qmm_block_variants(bits, waves, kgroups, nt):
             run_small_linear(M, N, K, bits, group, "f16", bias, lb.PATH_QMM, seed=bits + N)
 
 
+@pytest.mark.parametrize("rgroups,nt", [("1", "2"), ("2", "2"), ("1", "1")])
+@pytest.mark.parametrize("bits", [1, 3, 4, 6, 7])
+def test_qmm_bf16_block_variants(bits, rgroups, nt):
+    """bf16 MFMA blocks: 4 column waves of two column tiles in one row group
+    or two (64- and 128-row tiles, where LDS allows), and 4 waves of one
+    column tile; ragged shapes (rows past M, columns past N, a last K step of
+    32), one, two and four passes per step, zero-term sets cut short by the
+    end of K or of a K split."""
+    with lb.tuning(qmm_rgroups=int(rgroups), qmm_nt=int(nt)):
+        for (M, N, K, group, bias) in [(128, 300, 416, 32, True), (100, 520, 1024, 64, False),
+                                       (77, 257, 2080, 32, True), (128, 130, 2176, 128, False),
+                                       (64, 200, 1280, 256, True), (120, 640, 4096, 128, True)]:
+            run_small_linear(M, N, K, bits, group, "bf16", bias, lb.PATH_QMM, seed=bits + N)
+
+
 # (M, N, K, group, bias, blocks): the qmm_blocks override sets the block target
 # from which the schedule derives the K split (2 to 8 splits here; 0 = the
 # default target).
