@@ -129,6 +129,16 @@ hipError_t launch_qmm_b4(const QmmParams&, const QmmLaunch&, int act, hipStream_
 hipError_t launch_qmm_b5(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b6(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
 hipError_t launch_qmm_b7(const QmmParams&, const QmmLaunch&, int act, hipStream_t);
+// The small-M MFMA kernel (1 <= M <= 16, fp16 activations): blocks of
+// 16*nt columns (nt 1 or 2) over all of K, `waves` (4, 8 or 16) waves per
+// block splitting the K steps; no workspace, one launch.
+hipError_t launch_qmm_small_b1(const QmmParams&, int nt, int waves, hipStream_t);
+hipError_t launch_qmm_small_b2(const QmmParams&, int nt, int waves, hipStream_t);
+hipError_t launch_qmm_small_b3(const QmmParams&, int nt, int waves, hipStream_t);
+hipError_t launch_qmm_small_b4(const QmmParams&, int nt, int waves, hipStream_t);
+hipError_t launch_qmm_small_b5(const QmmParams&, int nt, int waves, hipStream_t);
+hipError_t launch_qmm_small_b6(const QmmParams&, int nt, int waves, hipStream_t);
+hipError_t launch_qmm_small_b7(const QmmParams&, int nt, int waves, hipStream_t);
 // The bf16 kernel's main launch (code operands; 4 column waves, nt == 2,
 // one K group); launch_qmm_b<bits> calls it and adds the split-K reduce.
 hipError_t launch_qmm_bf16_b1(const QmmParams&, const QmmLaunch&, hipStream_t);

@@ -125,7 +125,12 @@ const QmvLauncher kQmv[8] = {nullptr,
 // kernel from M = 5 (b = 4: 10.5 vs 11.2 us; b = 7: 12.7 vs 15.8 us): the
 // decode kernel serves four activation rows per pass and re-reads the
 // weights for the next four.
-inline int64_t qmv_max_m(int /*bits*/) { return 4; }
+// Largest M the decode kernel takes by default: fp32 activations always go
+// to it; fp16 from M = 4 and bf16 from M = 5 go to the MFMA kernels (the
+// small-M kernel for fp16 up to 16 rows; measured at K = N = 4096:
+// decode / small-M kernel at M = 2: 5.1 / 6.9 us, M = 4: 7.7 / 7.4,
+// M = 8: 11.3 / 7.9 at 4 bits, g = 128).
+inline int64_t qmv_max_m(lowbit_dtype act) { return act == LOWBIT_F16 ? 3 : 4; }
 static_assert(LOWBIT_MAX_MULTI <= lowbit::kQmvMaxProblems, "one launch serves every desc");
 
 typedef int (*QmvStageBytes)(int);
@@ -282,9 +287,20 @@ const QmmLauncher kQmm[8] = {nullptr,
                              lowbit::launch_qmm_b6,
                              lowbit::launch_qmm_b7};
 
+typedef hipError_t (*QmmSmallLauncher)(const lowbit::QmmParams&, int, int, hipStream_t);
+const QmmSmallLauncher kQmmSmall[8] = {nullptr,
+                                       lowbit::launch_qmm_small_b1,
+                                       lowbit::launch_qmm_small_b2,
+                                       lowbit::launch_qmm_small_b3,
+                                       lowbit::launch_qmm_small_b4,
+                                       lowbit::launch_qmm_small_b5,
+                                       lowbit::launch_qmm_small_b6,
+                                       lowbit::launch_qmm_small_b7};
+
 // Schedule of the MFMA kernel: block tile (16*mtt) x (16*nt*waves), K steps
 // of 128, and a K split that fills the CUs with one block each.
 struct QmmSchedule {
+  bool small;             // the small-M kernel (fields below: nt, waves only)
   int mtt, nt, waves, kgroups, rgroups;
   int64_t tiles_n, tiles_m, ksteps;
   int splits, ksteps_per_split;
@@ -334,9 +350,35 @@ constexpr int kQmmNarrowMaxSteps = 16;
 // (M = 64, K = N = 4096: 17.25 vs 16.8).
 constexpr int kQmmKGroupsMinSteps = 8;
 
+// Largest M of the small-M kernel (fp16 activations): it streams the weights
+// once per call whatever M is, while the tiled kernel pays a K split, its
+// reduce and a pipeline fill.
+constexpr int kQmmSmallMaxM = 16;
+
 QmmSchedule qmm_schedule(int bits, lowbit_dtype act, int64_t M, int64_t N, int64_t K) {
   QmmSchedule sc{};
   sc.rgroups = 1;
+  const int small_env = tuning(LOWBIT_TUNE_QMM_SMALL_M, kQmmSmallMaxM);
+  if (act == LOWBIT_F16 && M <= std::min(small_env, 16)) {
+    // blocks of 16 columns (32 when asked) over all of K; waves per block so
+    // that each takes at least two K steps
+    const int64_t ksteps = (K + 127) / 128;
+    sc.small = true;
+    sc.nt = tuning(LOWBIT_TUNE_QMM_NT, 1) == 2 ? 2 : 1;
+    sc.waves = ksteps >= 32 ? 16 : ksteps >= 16 ? 8 : 4;
+    const int wv_env = tuning(LOWBIT_TUNE_QMM_WAVES, 0);
+    if (wv_env == 4 || wv_env == 8 || wv_env == 16) sc.waves = wv_env;
+    if (sc.nt == 2 && sc.waves == 16) sc.waves = 8;
+    sc.mtt = 1;
+    sc.kgroups = 1;
+    sc.tiles_n = (N + 16 * sc.nt - 1) / (16 * sc.nt);
+    sc.tiles_m = 1;
+    sc.ksteps = ksteps;
+    sc.splits = 1;
+    sc.ksteps_per_split = static_cast<int>(ksteps);
+    sc.partial_bytes = 0;
+    return sc;
+  }
   sc.mtt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   const int mtt_env = tuning(LOWBIT_TUNE_QMM_MTT, 0);
   if (mtt_env == 1 || mtt_env == 2 || mtt_env == 4 || mtt_env == 8) sc.mtt = std::min(sc.mtt, mtt_env);
@@ -407,6 +449,22 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   // lane offsets from a per-step base
   if (act == LOWBIT_BF16 && (M * K * 2 > int64_t{0xffffffff} || N * (K * bits / 8) > int64_t{0xffffffff}))
     return fail(LOWBIT_ERR_UNSUPPORTED, "bf16 qmm: activations and packed codes must each be below 4 GiB");
+  if (sc.small) {
+    lowbit::QmmParams p{};
+    p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
+    p.M = static_cast<int>(M);
+    p.N = static_cast<int>(N);
+    p.K = static_cast<int>(K);
+    p.groups = static_cast<int>(K / group);
+    int gs = 0;
+    while ((1 << gs) < group) ++gs;
+    p.group_shift = gs;
+    p.row_bytes = K * bits / 8;
+    p.ksteps_per_split = static_cast<int>(sc.ksteps);
+    const hipError_t e = kQmmSmall[bits](p, sc.nt, sc.waves, stream);
+    if (e != hipSuccess) return hip_fail(e, "small-M qmm launch");
+    return LOWBIT_OK;
+  }
   lowbit::QmmParams p{};
   p.x = x; p.packed = packed; p.scales = scales; p.zeros = zeros; p.bias = bias; p.y = y;
   p.M = static_cast<int>(M);
@@ -543,7 +601,7 @@ lowbit_status lowbit_linear_path(const void* x, lowbit_dtype act_dtype, const ui
   bool use_qmm;
   if (path == LOWBIT_PATH_QMV) use_qmm = false;
   else if (path == LOWBIT_PATH_QMM) use_qmm = true;
-  else use_qmm = (M > qmv_max_m(bits)) && act_dtype != LOWBIT_F32;
+  else use_qmm = (M > qmv_max_m(act_dtype)) && act_dtype != LOWBIT_F32;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_qmm)
@@ -569,7 +627,7 @@ lowbit_status lowbit_linear_noalloc(const void* x, lowbit_dtype act_dtype, const
   if (st != LOWBIT_OK) return st;
   if (M == 0) return LOWBIT_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool use_qmm = (M > qmv_max_m(bits)) && act_dtype != LOWBIT_F32;
+  const bool use_qmm = (M > qmv_max_m(act_dtype)) && act_dtype != LOWBIT_F32;
   if (!use_qmm) return run_qmv(x, act_dtype, packed, scales, zeros, bias, y, bits, group, M, N, K, s);
   // the schedule lowbit_linear takes with a full workspace, its partial
   // planes in the library's device array

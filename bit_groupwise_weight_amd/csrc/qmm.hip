@@ -561,6 +561,145 @@ static hipError_t launch_act(const QmmParams& p, const QmmLaunch& l, hipStream_t
   }
 }
 
+// ---- small M (at most 16 rows), fp16 activations
+//
+// At a few rows the MFMA work is small and the time goes to streaming the
+// packed weights, so the block shape follows the decode kernel: a block owns
+// 16*NT columns over ALL of K (no K split across blocks, no second kernel),
+// its WV waves take contiguous ranges of K steps, and each wave loads what
+// it needs straight into registers -- per step and lane its 32-code run of
+// each column tile (the run mapping above), the run's scale and zero, and
+// the four A fragments of row fr (rows past M repeat row M-1 and are never
+// stored).  Loads go two steps at a time, one chunk ahead of the MFMAs.
+// The waves' 16 x 16*NT partial tiles are added through LDS in wave order
+// (fixed), the bias is added and the result rounded once.
+template <int BITS, int NT, int WV>
+__global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
+  constexpr int CH = 2;                        // K steps per load chunk
+  __shared__ float4_t red[WV][NT][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int fr = lane & 15;
+  const int g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * (16 * NT);
+  const int ksteps = (p.K + QMM_BK - 1) / QMM_BK;
+  const int spw = (ksteps + WV - 1) / WV;      // steps per wave
+  const int s0 = min(ksteps, wave * spw);
+  const int s1 = min(ksteps, s0 + spw);
+  const _Float16* xrow = static_cast<const _Float16*>(p.x) + static_cast<int64_t>(min(fr, p.M - 1)) * p.K;
+  const uint8_t* crow[NT];
+  const uint16_t* srow[NT];
+  const uint16_t* zrow[NT];
+  bool nok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt + fr;
+    nok[nt] = n < p.N;
+    const int nc = min(n, p.N - 1);
+    crow[nt] = p.packed + static_cast<int64_t>(nc) * p.row_bytes;
+    srow[nt] = static_cast<const uint16_t*>(p.scales) + static_cast<int64_t>(nc) * p.groups;
+    zrow[nt] = static_cast<const uint16_t*>(p.zeros) + static_cast<int64_t>(nc) * p.groups;
+  }
+
+  struct Step {
+    uint4 a[4];
+    uint32_t w[NT][BITS];
+    ScaleZero sz[NT];
+  };
+  // step j: this lane's run starts at K position kr; a run past K (ragged
+  // last step) or past the wave's range contributes zero operands
+  auto load = [&](int j, Step& S) {
+    const int kr = j * QMM_BK + 32 * g;
+    const bool ok = j < s1 && kr < p.K;
+    const int kc = ok ? kr : 0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xrow + kc + 8 * ks);
+      S.a[ks] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      load_run_words<BITS>(crow[nt] + (kc >> 3) * BITS, S.w[nt]);
+      const uint32_t live = (ok && nok[nt]) ? 0xffffu : 0u;
+      const uint32_t sb = srow[nt][kc >> p.group_shift] & live;
+      const uint32_t zb = zrow[nt][kc >> p.group_shift] & live;
+      S.sz[nt].s = 0.f;
+      S.sz[nt].z = 0.f;
+      S.sz[nt].s2 = sb * 0x10001u;
+      S.sz[nt].z2 = zb * 0x10001u;
+    }
+  };
+  float4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Step& S) {
+    static_for<4>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = mfma16x16x32<ACT_F16>(S.a[ks], dequant_ksub<BITS, ACT_F16, ks>(S.w[nt], S.sz[nt]), acc[nt]);
+    });
+  };
+
+  Step buf[2][CH];
+  if (s0 < s1) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) load(s0 + i, buf[0][i]);
+  }
+  for (int j = s0; j < s1; j += 2 * CH) {      // wave-uniform bounds
+    if (j + CH < s1) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) load(j + CH + i, buf[1][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) compute(buf[0][i]);
+    if (j + CH >= s1) break;
+    if (j + 2 * CH < s1) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) load(j + 2 * CH + i, buf[0][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) compute(buf[1][i]);
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) red[wave][nt][lane] = acc[nt];
+  __syncthreads();
+  // wave nt (< NT) adds the column tile's WV partial tiles in wave order
+  if (wave < NT) {
+    float4_t v = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < WV; ++w) v += red[w][wave][lane];
+    const int n = n0 + 16 * wave + fr;
+    if (n < p.N) {
+      const float b = p.bias ? load_act<ACT_F16>(p.bias, n) : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * g + r;
+        if (m < p.M) store_act<ACT_F16>(p.y, static_cast<int64_t>(m) * p.N + n, v[r] + b);
+      }
+    }
+  }
+}
+
+template <int NT>
+static hipError_t launch_small_nt(const QmmParams& p, int waves, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p.N + 16 * NT - 1) / (16 * NT)));
+  switch (waves) {
+    case 4: qmm_small_kernel<LOWBIT_BITS, NT, 4><<<grid, dim3(256), 0, s>>>(p); break;
+    case 8: qmm_small_kernel<LOWBIT_BITS, NT, 8><<<grid, dim3(512), 0, s>>>(p); break;
+    case 16:
+      if constexpr (NT == 1) {   // 1024 threads leave 128 registers a lane: one column tile
+        qmm_small_kernel<LOWBIT_BITS, NT, 16><<<grid, dim3(1024), 0, s>>>(p);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 #define LOWBIT_CAT2(a, b) a##b
 #define LOWBIT_CAT(a, b) LOWBIT_CAT2(a, b)
 hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLaunch& l, int act,
@@ -586,4 +725,15 @@ hipError_t LOWBIT_CAT(launch_qmm_b, LOWBIT_BITS)(const QmmParams& p, const QmmLa
   return hipGetLastError();
 }
 
+}  // namespace lowbit
+
+namespace lowbit {
+hipError_t LOWBIT_CAT(launch_qmm_small_b, LOWBIT_BITS)(const QmmParams& p, int nt, int waves, hipStream_t s) {
+  if (p.M < 1 || p.M > 16) return hipErrorInvalidValue;
+  switch (nt) {
+    case 1: return launch_small_nt<1>(p, waves, s);
+    case 2: return launch_small_nt<2>(p, waves, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 }  // namespace lowbit

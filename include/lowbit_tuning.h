@@ -31,7 +31,9 @@ typedef enum lowbit_tuning_key {
   LOWBIT_TUNE_QMM_NT = 5,       /* fp16 MFMA kernel: 1 or 2 column tiles per wave   */
   LOWBIT_TUNE_QMM_WAVES = 6,    /* fp16 MFMA kernel, one K group: 4 or 8 waves      */
   LOWBIT_TUNE_QMM_RGROUPS = 7,  /* bf16 MFMA kernel: 1 or 2 row groups of 4 waves   */
-  LOWBIT_TUNE_COUNT = 8
+  LOWBIT_TUNE_QMM_SMALL_M = 8,  /* fp16: largest M of the small-M MFMA kernel (1-16;
+                                   1 = not used)                                    */
+  LOWBIT_TUNE_COUNT = 9
 } lowbit_tuning_key;
 
 /* Set (value > 0) or clear (value == 0) one override.  LOWBIT_ERR_INVALID_ARG

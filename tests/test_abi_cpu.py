@@ -140,7 +140,7 @@ def test_quantize_validation(lowbit_lib, args, status):
 
 
 def test_tuning_validation(lowbit_lib):
-    assert lowbit_lib.lowbit_set_tuning(8, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(9, 1) == INVALID
     assert lowbit_lib.lowbit_set_tuning(7, 2) == OK and lowbit_lib.lowbit_set_tuning(7, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(-1, 1) == INVALID
     assert lowbit_lib.lowbit_set_tuning(0, -2) == INVALID
@@ -192,7 +192,9 @@ def test_probe_chase_validation(lowbit_lib, args, status):
     (64, 4096, 4096, 4, 64, "f16", 8),        # 4 steps per block: one K group
     (64, 4096, 14336, 4, 64, "f16", 2),       # 16 steps per block: two K groups
     (128, 4096, 14336, 7, 128, "f16", 2),     # 7 bits: 4-wave blocks
-    (16, 4096, 4096, 4, 64, "f16", 8),
+    (16, 4096, 4096, 4, 64, "f16", 0),        # fp16 at M <= 16: the small-M kernel, no split
+    (32, 4096, 4096, 4, 64, "f16", 8),        # 32-row tiles: split in 8
+    (16, 4096, 4096, 4, 64, "bf16", 8),       # bf16 at 16 rows: the tiled kernel
 ])
 def test_mfma_schedule_workspace(lowbit_lib, M, K, N, bits, group, dtype, planes):
     """The MFMA schedule on a 256-CU device, seen through the workspace it asks

@@ -191,10 +191,31 @@ def test_qmv_small(bits, act):
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", range(1, 8))
 def test_qmm_small(bits, act):
-    for (M, N, K, group, bias) in [(16, 64, 256, 64, False), (17, 130, 352, 32, True),
-                                   (64, 70, 768, 256, True), (100, 200, 384, 128, False),
-                                   (1, 5, 64, 32, True), (130, 64, 1024, 64, True)]:
-        run_small_linear(M, N, K, bits, group, act, bias, lb.PATH_QMM, seed=bits + M + K)
+    # fp16 at M <= 16 runs the small-M kernel; with qmm_small_m=1 the tiled
+    # kernel takes those rows too
+    for small_m in (0, 1):
+        if small_m and act != "f16":
+            continue
+        with lb.tuning(qmm_small_m=small_m):
+            for (M, N, K, group, bias) in [(16, 64, 256, 64, False), (17, 130, 352, 32, True),
+                                           (64, 70, 768, 256, True), (100, 200, 384, 128, False),
+                                           (1, 5, 64, 32, True), (130, 64, 1024, 64, True)]:
+                run_small_linear(M, N, K, bits, group, act, bias, lb.PATH_QMM, seed=bits + M + K)
+
+
+@pytest.mark.parametrize("nt,waves", [("1", "0"), ("1", "4"), ("2", "8"), ("1", "16")])
+@pytest.mark.parametrize("bits", range(1, 8))
+def test_qmm_small_m_kernel(bits, nt, waves):
+    """The small-M fp16 kernel: every M from 1 to 16, columns past N, a last
+    K step of 32, a single 32-long run, K ranges that leave waves without
+    steps or with an odd number of two-step chunks, every group size."""
+    with lb.tuning(qmm_small_m=16, qmm_nt=int(nt), qmm_waves=int(waves)):
+        for (M, N, K, group, bias) in [(1, 40, 416, 32, True), (2, 300, 1024, 64, False),
+                                       (3, 17, 32, 32, True), (4, 130, 2176, 128, True),
+                                       (5, 64, 768, 256, False), (8, 257, 4096, 128, True),
+                                       (11, 96, 1280, 256, True), (13, 33, 640, 32, False),
+                                       (16, 200, 3328, 64, True), (16, 48, 14336, 128, False)]:
+            run_small_linear(M, N, K, bits, group, "f16", bias, lb.PATH_QMM, seed=bits + 7 * M + N)
 
 
 @pytest.mark.parametrize("act", ["f16", "bf16", "f32"])
