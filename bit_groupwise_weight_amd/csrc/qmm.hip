@@ -564,19 +564,28 @@ static hipError_t launch_act(const QmmParams& p, const QmmLaunch& l, hipStream_t
 // ---- small M (at most 16 rows), fp16 activations
 //
 // At a few rows the MFMA work is small and the time goes to streaming the
-// packed weights, so the block shape follows the decode kernel: a block owns
-// 16*NT columns over ALL of K (no K split across blocks, no second kernel),
-// its WV waves take contiguous ranges of K steps, and each wave loads what
-// it needs straight into registers -- per step and lane its 32-code run of
-// each column tile (the run mapping above), the run's scale and zero, and
-// the four A fragments of row fr (rows past M repeat row M-1 and are never
-// stored).  Loads go two steps at a time, one chunk ahead of the MFMAs.
+// packed weights -- and, on this hardware, to the number of vector-memory
+// instructions each CU must issue (a wave stalls while the address unit
+// works through its queue).  So the block shape follows the decode kernel
+// and every load is as wide as it can be: a block owns 16*NT columns over
+// ALL of K (no K split across blocks, no second kernel), its WV waves take
+// contiguous ranges of K steps, two steps per chunk, one chunk in flight
+// ahead of the MFMAs.  Per step a wave loads
+//   * the activation rows, 4 rows x 256 contiguous bytes per instruction
+//     (MR instructions: rows past M repeat row M-1), which it writes to its
+//     own LDS slice (swizzled as the tiled kernels' stage) and reads back as
+//     A fragments -- one wave writes and reads, so no barrier;
+//   * per column tile, this lane's 32-code run (the run mapping above);
+// and per chunk the scales and zeros its runs need, spread over the four
+// lanes of each column (one 2-byte load per lane per chunk at group >= 128)
+// and handed to the lanes that use them by ds_bpermute.
 // The waves' 16 x 16*NT partial tiles are added through LDS in wave order
 // (fixed), the bias is added and the result rounded once.
-template <int BITS, int NT, int WV>
+template <int BITS, int NT, int WV, int MR>
 __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
   constexpr int CH = 2;                        // K steps per load chunk
   __shared__ float4_t red[WV][NT][64];
+  __shared__ uint4 xs[WV][4 * MR * 16];        // per wave: 4*MR rows x 16 chunks of 16 bytes
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int fr = lane & 15;
@@ -587,7 +596,21 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
   const int spw = (ksteps + WV - 1) / WV;      // steps per wave
   const int s0 = min(ksteps, wave * spw);
   const int s1 = min(ksteps, s0 + spw);
-  const _Float16* xrow = static_cast<const _Float16*>(p.x) + static_cast<int64_t>(min(fr, p.M - 1)) * p.K;
+  const int gsh = p.group_shift;
+  // groups per step a lane's runs fall in: R = 128 / min(group, 128)
+  const int rsh = gsh >= 7 ? 0 : 7 - gsh;      // log2 R
+  const int R = 1 << rsh;
+  // activation pieces: piece i of a step is row min(4i + l/16, M-1), 16
+  // bytes at K offset 8 (l%16); it lands at chunk (l%16) ^ swizzle(row)
+  const _Float16* xp[MR];
+  int xdst[MR];
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+    const int r = 4 * i + g;
+    xp[i] = static_cast<const _Float16*>(p.x) + static_cast<int64_t>(min(r, p.M - 1)) * p.K + 8 * fr;
+    xdst[i] = r * 16 + (fr ^ stage_swizzle(r));
+  }
+  const int arow = min(fr, 4 * MR - 1);        // A fragment row (rows >= M hold row M-1)
   const uint8_t* crow[NT];
   const uint16_t* srow[NT];
   const uint16_t* zrow[NT];
@@ -602,65 +625,107 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
     zrow[nt] = static_cast<const uint16_t*>(p.zeros) + static_cast<int64_t>(nc) * p.groups;
   }
 
-  struct Step {
-    uint4 a[4];
-    uint32_t w[NT][BITS];
-    ScaleZero sz[NT];
+  // One chunk (steps j0, j0 + 1).  Scale / zero slots: slot q of the chunk
+  // is group ((j0 + q / R) * 128 + (q % R) * min(group, 128)) >> gsh, q <
+  // 2R; value v < 4R is (v < 2R ? scale : zero) of slot v % 2R, held by
+  // lane group v % 4 of the column in register v / 4.
+  struct Chunk {
+    uint4 x[CH][MR];
+    uint32_t w[CH][NT][BITS];
+    uint32_t sz[NT][4];                        // this lane's values, by register (R of them)
   };
-  // step j: this lane's run starts at K position kr; a run past K (ragged
-  // last step) or past the wave's range contributes zero operands
-  auto load = [&](int j, Step& S) {
-    const int kr = j * QMM_BK + 32 * g;
-    const bool ok = j < s1 && kr < p.K;
-    const int kc = ok ? kr : 0;
+  auto load = [&](int j0, Chunk& C) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(xrow + kc + 8 * ks);
-      S.a[ks] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+    for (int t = 0; t < CH; ++t) {
+      const int j = j0 + t;
+      const int kb = j * QMM_BK;
+      const bool step_ok = j < s1;
+      // activation pieces (K offsets past K read zero; K is a multiple of
+      // 32, so a piece is wholly inside or outside)
+      const bool kin = step_ok && kb + 8 * fr < p.K;
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xp[i] + (kin ? kb : 0));
+        C.x[t][i] = kin ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
+      const int kr = kb + 32 * g;              // this lane's run
+      const int kc = (step_ok && kr < p.K) ? kr : 0;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) load_run_words<BITS>(crow[nt] + (kc >> 3) * BITS, C.w[t][nt]);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      load_run_words<BITS>(crow[nt] + (kc >> 3) * BITS, S.w[nt]);
-      const uint32_t live = (ok && nok[nt]) ? 0xffffu : 0u;
-      const uint32_t sb = srow[nt][kc >> p.group_shift] & live;
-      const uint32_t zb = zrow[nt][kc >> p.group_shift] & live;
-      S.sz[nt].s = 0.f;
-      S.sz[nt].z = 0.f;
-      S.sz[nt].s2 = sb * 0x10001u;
-      S.sz[nt].z2 = zb * 0x10001u;
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) C.sz[nt][i] = 0u;
+      if (i < R) {                              // wave-uniform
+        const int v = 4 * i + g;
+        const int q = v & (2 * R - 1);
+        const int kq = (j0 + (q >> rsh)) * QMM_BK + ((q & (R - 1)) << (gsh >= 7 ? 7 : gsh));
+        const bool ok = j0 + (q >> rsh) < s1 && kq < p.K;
+        const int gi = ok ? (kq >> gsh) : 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t b = (v < 2 * R ? srow[nt] : zrow[nt])[gi];
+          C.sz[nt][i] = (ok && nok[nt]) ? b : 0u;
+        }
+      }
     }
   };
   float4_t acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Step& S) {
-    static_for<4>([&](auto kc) {
-      constexpr int ks = decltype(kc)::value;
+  auto compute = [&](const Chunk& C) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = mfma16x16x32<ACT_F16>(S.a[ks], dequant_ksub<BITS, ACT_F16, ks>(S.w[nt], S.sz[nt]), acc[nt]);
-    });
+    for (int t = 0; t < CH; ++t) {
+      // this step's activation rows through the wave's LDS slice
+#pragma unroll
+      for (int i = 0; i < MR; ++i) xs[wave][xdst[i]] = C.x[t][i];
+      uint4 a[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a[ks] = xs[wave][arow * 16 + ((4 * g + ks) ^ stage_swizzle(arow))];
+      // scale and zero of this lane's run, slot q = t R + 32 g / min(group,
+      // 128): the scale is value q, the zero value 2R + q, each held by
+      // lane group (v % 4) of the column in register v / 4 -- a register
+      // index that is the same for every lane (R = 4: t and 2 + t, held by
+      // the lane itself; R = 2: 0 and 1; R = 1: 0 and 0)
+      const int q = t * R + ((32 * g) >> (gsh >= 7 ? 7 : gsh));
+      const int rs = R == 4 ? t : 0;
+      const int rz = R == 4 ? 2 + t : R == 2 ? 1 : 0;
+      ScaleZero sz[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        uint32_t sv = C.sz[nt][0], zv = C.sz[nt][0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+          sv = rs == i ? C.sz[nt][i] : sv;
+          zv = rz == i ? C.sz[nt][i] : zv;
+        }
+        if (R < 4) {                            // wave-uniform
+          sv = __builtin_amdgcn_ds_bpermute(4 * (fr + 16 * (q & 3)), sv);
+          zv = __builtin_amdgcn_ds_bpermute(4 * (fr + 16 * ((2 * R + q) & 3)), zv);
+        }
+        sz[nt].s = 0.f;
+        sz[nt].z = 0.f;
+        sz[nt].s2 = (sv & 0xffffu) * 0x10001u;
+        sz[nt].z2 = (zv & 0xffffu) * 0x10001u;
+      }
+      static_for<4>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = mfma16x16x32<ACT_F16>(a[ks], dequant_ksub<BITS, ACT_F16, ks>(C.w[t][nt], sz[nt]), acc[nt]);
+      });
+    }
   };
 
-  Step buf[2][CH];
-  if (s0 < s1) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) load(s0 + i, buf[0][i]);
-  }
+  Chunk buf[2];
+  if (s0 < s1) load(s0, buf[0]);
   for (int j = s0; j < s1; j += 2 * CH) {      // wave-uniform bounds
-    if (j + CH < s1) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) load(j + CH + i, buf[1][i]);
-    }
-#pragma unroll
-    for (int i = 0; i < CH; ++i) compute(buf[0][i]);
+    if (j + CH < s1) load(j + CH, buf[1]);
+    compute(buf[0]);
     if (j + CH >= s1) break;
-    if (j + 2 * CH < s1) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) load(j + 2 * CH + i, buf[0][i]);
-    }
-#pragma unroll
-    for (int i = 0; i < CH; ++i) compute(buf[1][i]);
+    if (j + 2 * CH < s1) load(j + 2 * CH, buf[0]);
+    compute(buf[1]);
   }
 
 #pragma unroll
@@ -683,21 +748,29 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
   }
 }
 
-template <int NT>
-static hipError_t launch_small_nt(const QmmParams& p, int waves, hipStream_t s) {
+template <int NT, int MR>
+static hipError_t launch_small_mr(const QmmParams& p, int waves, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p.N + 16 * NT - 1) / (16 * NT)));
+  if (waves == 16 && MR > 1) waves = 8;        // past 4 rows registers allow 8 waves
   switch (waves) {
-    case 4: qmm_small_kernel<LOWBIT_BITS, NT, 4><<<grid, dim3(256), 0, s>>>(p); break;
-    case 8: qmm_small_kernel<LOWBIT_BITS, NT, 8><<<grid, dim3(512), 0, s>>>(p); break;
+    case 4: qmm_small_kernel<LOWBIT_BITS, NT, 4, MR><<<grid, dim3(256), 0, s>>>(p); break;
+    case 8: qmm_small_kernel<LOWBIT_BITS, NT, 8, MR><<<grid, dim3(512), 0, s>>>(p); break;
     case 16:
-      if constexpr (NT == 1) {   // 1024 threads leave 128 registers a lane: one column tile
-        qmm_small_kernel<LOWBIT_BITS, NT, 16><<<grid, dim3(1024), 0, s>>>(p);
+      if constexpr (NT == 1 && MR == 1) {   // 1024 threads leave 128 registers a lane
+        qmm_small_kernel<LOWBIT_BITS, NT, 16, MR><<<grid, dim3(1024), 0, s>>>(p);
         break;
       }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int NT>
+static hipError_t launch_small_nt(const QmmParams& p, int waves, hipStream_t s) {
+  if (p.M <= 4) return launch_small_mr<NT, 1>(p, waves, s);
+  if (p.M <= 8) return launch_small_mr<NT, 2>(p, waves, s);
+  return launch_small_mr<NT, 4>(p, waves, s);
 }
 
 #define LOWBIT_CAT2(a, b) a##b
