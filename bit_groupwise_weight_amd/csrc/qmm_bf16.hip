@@ -26,9 +26,9 @@
 // codes (and ones) of the other groups' lane groups masked to zero, so that
 // P and X of a pass cover exactly one group.
 //
-// The rescale y += s * P: the row tiles go in chunks of two; a chunk's P is
-// rescaled by the VALU while the MFMAs of the next chunk run (two P
-// buffers).  The zero term z * X is itself an MFMA product: X of a row
+// The rescale y += s * P: the row tiles go in chunks of up to four; with an
+// even chunk count a chunk's P is rescaled by the VALU while the MFMAs of
+// the next chunk run (two P buffers).  The zero term z * X is itself an MFMA product: X of a row
 // tile is computed once per block (by one wave), split exactly into three
 // bf16 truncations and written to LDS; every four windows (pass of a step)
 // one MFMA per output tile adds sum over windows and pieces of X * z.
@@ -160,8 +160,10 @@ __global__ __launch_bounds__(64 * WC * WR, 1) void qmm_bf16_kernel(QmmParams p) 
   static_assert(MTW >= 1 && MTT % WR == 0, "row groups");
   // row tiles per chunk: the group sums P of one chunk are in flight at a
   // time, double-buffered so that a chunk's rescale runs under the MFMAs of
-  // the next (with an even chunk count per pass; otherwise right away)
-  constexpr int MC = MTW < 2 ? MTW : 2;
+  // the next (with an even chunk count per pass; otherwise right away).
+  // Chunks of four: a slot's 9 MFMAs cover the LDS reads of the next slot
+  // (chunks of two: 3-5 % slower at M = 128, A/B on one box)
+  constexpr int MC = MTW < 4 ? MTW : 4;
   constexpr int NCH = MTW / MC;               // chunks per pass
   constexpr bool DEFER = NCH % 2 == 0;
   constexpr int LPP = 4 / NP;                 // lane groups per pass
