@@ -126,11 +126,11 @@ const QmvLauncher kQmv[8] = {nullptr,
 // decode kernel serves four activation rows per pass and re-reads the
 // weights for the next four.
 // Largest M the decode kernel takes by default: fp32 activations always go
-// to it; fp16 from M = 4 and bf16 from M = 5 go to the MFMA kernels (the
-// small-M kernel for fp16 up to 16 rows; measured at K = N = 4096:
-// decode / small-M kernel at M = 2: 5.1 / 6.9 us, M = 4: 7.7 / 7.4,
-// M = 8: 11.3 / 7.9 at 4 bits, g = 128).
-inline int64_t qmv_max_m(lowbit_dtype act) { return act == LOWBIT_F16 ? 3 : 4; }
+// to it; fp16 from M = 3 and bf16 from M = 5 go to the MFMA kernels (the
+// small-M kernel for fp16 up to 16 rows; measured at K = N = 4096, decode /
+// small-M kernel, us: M = 2 5.1-6.8 / 5.4-7.6, M = 4 7.3-9.9 / 5.5-7.4,
+// M = 8 10.8-16.4 / 6.6-8.2).
+inline int64_t qmv_max_m(lowbit_dtype act) { return act == LOWBIT_F16 ? 2 : 4; }
 static_assert(LOWBIT_MAX_MULTI <= lowbit::kQmvMaxProblems, "one launch serves every desc");
 
 typedef int (*QmvStageBytes)(int);

@@ -629,10 +629,14 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
   // is group ((j0 + q / R) * 128 + (q % R) * min(group, 128)) >> gsh, q <
   // 2R; value v < 4R is (v < 2R ? scale : zero) of slot v % 2R, held by
   // lane group v % 4 of the column in register v / 4.
+  // (loaded values are kept raw: a select on a loaded value would make the
+  // load wait at once; the masks are applied where the values are used)
   struct Chunk {
     uint4 x[CH][MR];
+    uint32_t xok[CH];                          // activation pieces inside K: all ones, else 0
     uint32_t w[CH][NT][BITS];
     uint32_t sz[NT][4];                        // this lane's values, by register (R of them)
+    uint32_t szok[NT][4];
   };
   auto load = [&](int j0, Chunk& C) {
 #pragma unroll
@@ -643,11 +647,9 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
       // activation pieces (K offsets past K read zero; K is a multiple of
       // 32, so a piece is wholly inside or outside)
       const bool kin = step_ok && kb + 8 * fr < p.K;
+      C.xok[t] = kin ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xp[i] + (kin ? kb : 0));
-        C.x[t][i] = kin ? v : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int i = 0; i < MR; ++i) C.x[t][i] = *reinterpret_cast<const uint4*>(xp[i] + (kin ? kb : 0));
       const int kr = kb + 32 * g;              // this lane's run
       const int kc = (step_ok && kr < p.K) ? kr : 0;
 #pragma unroll
@@ -656,7 +658,10 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) C.sz[nt][i] = 0u;
+      for (int nt = 0; nt < NT; ++nt) {
+        C.sz[nt][i] = 0u;
+        C.szok[nt][i] = 0u;
+      }
       if (i < R) {                              // wave-uniform
         const int v = 4 * i + g;
         const int q = v & (2 * R - 1);
@@ -665,8 +670,8 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
         const int gi = ok ? (kq >> gsh) : 0;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const uint32_t b = (v < 2 * R ? srow[nt] : zrow[nt])[gi];
-          C.sz[nt][i] = (ok && nok[nt]) ? b : 0u;
+          C.sz[nt][i] = (v < 2 * R ? srow[nt] : zrow[nt])[gi];
+          C.szok[nt][i] = (ok && nok[nt]) ? 0xffffu : 0u;
         }
       }
     }
@@ -679,7 +684,10 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
     for (int t = 0; t < CH; ++t) {
       // this step's activation rows through the wave's LDS slice
 #pragma unroll
-      for (int i = 0; i < MR; ++i) xs[wave][xdst[i]] = C.x[t][i];
+      for (int i = 0; i < MR; ++i) {
+        const uint32_t m = C.xok[t];
+        xs[wave][xdst[i]] = make_uint4(C.x[t][i].x & m, C.x[t][i].y & m, C.x[t][i].z & m, C.x[t][i].w & m);
+      }
       uint4 a[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) a[ks] = xs[wave][arow * 16 + ((4 * g + ks) ^ stage_swizzle(arow))];
@@ -694,11 +702,12 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
       ScaleZero sz[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        uint32_t sv = C.sz[nt][0], zv = C.sz[nt][0];
+        uint32_t sv = C.sz[nt][0] & C.szok[nt][0], zv = sv;
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
-          sv = rs == i ? C.sz[nt][i] : sv;
-          zv = rz == i ? C.sz[nt][i] : zv;
+          const uint32_t vi = C.sz[nt][i] & C.szok[nt][i];
+          sv = rs == i ? vi : sv;
+          zv = rz == i ? vi : zv;
         }
         if (R < 4) {                            // wave-uniform
           sv = __builtin_amdgcn_ds_bpermute(4 * (fr + 16 * (q & 3)), sv);
@@ -751,12 +760,22 @@ __global__ __launch_bounds__(64 * WV) void qmm_small_kernel(QmmParams p) {
 template <int NT, int MR>
 static hipError_t launch_small_mr(const QmmParams& p, int waves, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p.N + 16 * NT - 1) / (16 * NT)));
-  if (waves == 16 && MR > 1) waves = 8;        // past 4 rows registers allow 8 waves
+  // instances whose registers would spill are not built: past 4 rows or 6
+  // bits no 16-wave blocks; at 7 bits, 32 columns and 16 rows 4 waves
+  constexpr bool w16 = NT == 1 && MR == 1 && LOWBIT_BITS <= 6;
+  constexpr bool w8 = !(NT == 2 && MR == 4 && LOWBIT_BITS > 6);
+  if (waves == 16 && !w16) waves = 8;
+  if (waves == 8 && !w8) waves = 4;
   switch (waves) {
     case 4: qmm_small_kernel<LOWBIT_BITS, NT, 4, MR><<<grid, dim3(256), 0, s>>>(p); break;
-    case 8: qmm_small_kernel<LOWBIT_BITS, NT, 8, MR><<<grid, dim3(512), 0, s>>>(p); break;
+    case 8:
+      if constexpr (w8) {
+        qmm_small_kernel<LOWBIT_BITS, NT, 8, MR><<<grid, dim3(512), 0, s>>>(p);
+        break;
+      }
+      return hipErrorInvalidValue;
     case 16:
-      if constexpr (NT == 1 && MR == 1) {   // 1024 threads leave 128 registers a lane
+      if constexpr (w16) {   // 1024 threads leave 128 registers a lane
         qmm_small_kernel<LOWBIT_BITS, NT, 16, MR><<<grid, dim3(1024), 0, s>>>(p);
         break;
       }

@@ -78,7 +78,7 @@ typedef enum lowbit_dtype {
 
 /* Which kernel family lowbit_linear_path runs. */
 typedef enum lowbit_path {
-  LOWBIT_PATH_AUTO = 0,  /* qmv for fp32 activations, fp16 at M <= 3 and
+  LOWBIT_PATH_AUTO = 0,  /* qmv for fp32 activations, fp16 at M <= 2 and
                             bf16 at M <= 4; qmm otherwise */
   LOWBIT_PATH_QMV = 1,   /* decode matrix-vector kernel, any M              */
   LOWBIT_PATH_QMM = 2    /* MFMA kernels, fp16/bf16 only (fp16 at M <= 16:
