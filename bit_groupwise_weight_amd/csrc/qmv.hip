@@ -15,15 +15,14 @@
 //     each 32-code run's activation sum X; activation
 //     loads are issued before the weight loads so the stage is ready while the
 //     weights are still in flight;
-//   * codes reach the dot products as exact values: fp16 codes by OR-ing
-//     exponent fields (see qmv_plan.h), which gives 2^(10-o) + q, and one
-//     packed fp16 subtract of 2^(10-o) per pair, then v_dot2_f32_f16 (at 2
-//     and 4 bits as fp16 subnormals q * 2^(o-24), one accumulator per bit
-//     offset, without the subtract); bf16
-//     codes through the fp8 conversion (a code below 16 in a byte is the
-//     e4m3 value q * 2^-9) or, above 4 bits, through fp32; fp32 converts
-//     each code.  Only the products x*q enter the fp32 sums, so their
-//     rounding is relative to sum |x*q| and not to a large constant part;
+//   * codes reach the dot products as exact values: fp16 codes as fp16
+//     subnormals q * 2^(o-24), two per 32-bit word at one bit offset o of
+//     their halves (funnel-shift windows or byte permutes, qmv_plan.h),
+//     masked with one AND and multiplied with one v_dot2_f32_f16, one fp32
+//     accumulator per offset; bf16 codes through the fp8 conversion (a code
+//     below 16 in a byte is the e4m3 value q * 2^-9) or, above 4 bits,
+//     through fp32; fp32 converts each code.  Only the products x*q enter
+//     the fp32 sums, so their rounding is relative to sum |x*q|;
 //   * per 32-code run (which never crosses a group):
 //       y += s * (sum_k x_k q_k) + z * X;
 //   * the R row partial sums of the lanes of a row group are combined with
@@ -38,10 +37,28 @@
 
 namespace lowbit {
 
+// The fp16 slot plan of a width (qmv_plan.h): funnel-shift windows for the
+// widths dividing 16 (at 1 bit, windows of 4 bits: four offsets to combine
+// instead of ten), byte permutes for the others.
+template <int BITS, bool PERM = (16 % BITS != 0)> struct F16Slots;
+template <int BITS> struct F16Slots<BITS, false> {
+  static constexpr int span = BITS == 1 ? 4 : f16_default_span<BITS>();
+  using Plan = F16Plan<BITS, span>;
+  static constexpr int n = Plan::n;
+  static constexpr int klo(int i) { return Plan::table.s[i].klo; }
+  static constexpr int khi(int i) { return Plan::table.s[i].khi; }
+};
+template <int BITS> struct F16Slots<BITS, true> {
+  using Plan = F16PermPlan<BITS>;
+  static constexpr int n = Plan::n;
+  static constexpr int klo(int i) { return Plan::table.s[i].klo; }
+  static constexpr int khi(int i) { return Plan::table.s[i].khi; }
+};
+
 // Raw activation words per 32-code run and staged words per run.
 template <int ACT> struct RawWords { static constexpr int n = (ACT == ACT_F32) ? 32 : 16; };
 template <int ACT, int BITS> struct StagedWords;
-template <int BITS> struct StagedWords<ACT_F16, BITS> { static constexpr int n = F16Plan<BITS>::n; };
+template <int BITS> struct StagedWords<ACT_F16, BITS> { static constexpr int n = F16Slots<BITS>::n; };
 template <int BITS> struct StagedWords<ACT_BF16, BITS> { static constexpr int n = 16; };
 template <int BITS> struct StagedWords<ACT_F32, BITS> { static constexpr int n = 32; };
 // uint4 quads per staged run: the words, then X, padded to 16 bytes.
@@ -53,11 +70,11 @@ template <int ACT, int BITS> struct RunQuads {
 
 template <int BITS, int I = 0>
 __device__ __forceinline__ void f16_stage_slots(const uint32_t* raw, uint32_t* out) {
-  if constexpr (I < F16Plan<BITS>::n) {
-    constexpr PairSlot s = F16Plan<BITS>::table.s[I];
+  if constexpr (I < F16Slots<BITS>::n) {
+    constexpr int klo = F16Slots<BITS>::klo(I), khi = F16Slots<BITS>::khi(I);
     uint32_t lo = 0, hi = 0;
-    if constexpr (s.klo >= 0) lo = (raw[s.klo >> 1] >> ((s.klo & 1) * 16)) & 0xffffu;
-    if constexpr (s.khi >= 0) hi = (raw[s.khi >> 1] >> ((s.khi & 1) * 16)) & 0xffffu;
+    if constexpr (klo >= 0) lo = (raw[klo >> 1] >> ((klo & 1) * 16)) & 0xffffu;
+    if constexpr (khi >= 0) hi = (raw[khi >> 1] >> ((khi & 1) * 16)) & 0xffffu;
     out[I] = lo | (hi << 16);
     f16_stage_slots<BITS, I + 1>(raw, out);
   }
@@ -88,93 +105,102 @@ __device__ __forceinline__ void stage_run(const uint32_t* raw, uint32_t* out) {
 
 // ------------------------------------------------------------------ dots --
 
-// The value unchanged, but held in a VGPR and opaque to constant folding.
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
-  asm("" : "+v"(v));
-  return v;
+// Bits [Q, Q + 32) of the run's code stream (zero past its end).
+template <int BITS, int Q>
+__device__ __forceinline__ uint32_t stream_word(const uint32_t* w) {
+  constexpr int d = Q / 32, sh = Q % 32;
+  if constexpr (d >= BITS) return 0u;
+  else if constexpr (sh == 0) return w[d];
+  else if constexpr (d + 1 < BITS) return __builtin_amdgcn_alignbit(w[d + 1], w[d], sh);
+  else return w[d] >> sh;
 }
 
-template <int BITS, int I = 0>
-__device__ __forceinline__ float f16_dot_slots(const uint32_t* w, const uint32_t* xs, float acc) {
-  if constexpr (I < F16Plan<BITS>::n) {
-    constexpr PairSlot s = F16Plan<BITS>::table.s[I];
-    uint32_t win;
-    if constexpr (s.shift == 0) {
-      win = w[s.word];
-    } else if constexpr (s.word + 1 < BITS) {
-      win = __builtin_amdgcn_alignbit(w[s.word + 1], w[s.word], s.shift);
-    } else {
-      win = w[s.word] >> s.shift;
-    }
-    constexpr uint32_t m = (1u << BITS) - 1u;
-    constexpr uint32_t mask = (s.klo >= 0 ? (m << s.olo) : 0u) |
-                              (s.khi >= 0 ? (m << (16 + s.ohi)) : 0u);
-    constexpr uint32_t mag = f16_magic_for_offset(s.olo) | (f16_magic_for_offset(s.ohi) << 16);
-    // mag lives in a VGPR so that the AND and the OR fuse into one
-    // v_and_or_b32 (a VOP3 form may read one scalar constant: the mask).
-    // Each half then reads 2^(10-o) + q exactly; subtracting 2^(10-o) is
-    // exact too (q < 2^(10-o)), which leaves the codes themselves.
-    const uint32_t v = (win & mask) | in_vgpr(mag);
-    constexpr _Float16 mlo = static_cast<_Float16>(1u << (10 - s.olo));
-    constexpr _Float16 mhi = static_cast<_Float16>(1u << (10 - s.ohi));
-    const half2_t q = __builtin_bit_cast(half2_t, v) - half2_t{mlo, mhi};
-    acc = dot2<ACT_F16>(xs[I], __builtin_bit_cast(uint32_t, q), acc);
-    return f16_dot_slots<BITS, I + 1>(w, xs, acc);
+// fp16: slot I of the plan (qmv_plan.h) as one word holding its two codes
+// at bit offset f16_slot_offset(I) of their halves, every other bit clear:
+// the halves read as the fp16 subnormals q * 2^(o-24).
+template <int BITS, int I>
+constexpr int f16_slot_offset() {
+  if constexpr (16 % BITS == 0) {
+    constexpr PairSlot s = F16Slots<BITS>::Plan::table.s[I];
+    static_assert(s.klo < 0 || s.khi < 0 || s.olo == s.ohi, "paired codes share their offset");
+    return s.klo >= 0 ? s.olo : s.ohi;
   } else {
-    return acc;
+    return F16PermPlan<BITS>::table.s[I].o;
   }
 }
 
-// Widths that divide 16 put the two codes of every slot at the same bit
-// offset o of their halves; at 2 and 4 bits (five and two offsets) the form
-// below is the cheaper one.  There the exponent field stays
-// zero: each half is the fp16 subnormal q * 2^(o-24), exact, and v_dot2
-// keeps subnormal inputs (fp16 denormals are on), so one AND and one dot2
-// per pair suffice.  Products of one offset share an fp32 accumulator;
-// the accumulators are combined with exact power-of-two steps
-// (sum x*q = sum_o acc_o * 2^(24-o)), so the rounding stays relative to
-// sum |x*q| as in the general form.
-template <int BITS> struct F16SubPlan {
-  static constexpr bool on = BITS == 2 || BITS == 4;   // (1 bit: ten offsets, no gain)
-  static constexpr int noff = F16Plan<BITS>::span / BITS;   // offsets 0, b, 2b, ...
+template <int BITS, int I>
+__device__ __forceinline__ uint32_t f16_slot_word(const uint32_t* w) {
+  constexpr uint32_t m = (1u << BITS) - 1u;
+  if constexpr (16 % BITS == 0) {
+    // funnel-shift window of word s.word
+    constexpr PairSlot s = F16Slots<BITS>::Plan::table.s[I];
+    constexpr uint32_t mask = (s.klo >= 0 ? (m << s.olo) : 0u) |
+                              (s.khi >= 0 ? (m << (16 + s.ohi)) : 0u);
+    return stream_word<BITS, 32 * s.word + s.shift>(w) & mask;
+  } else {
+    // two halves gathered by one byte permute
+    constexpr PermSlot s = F16PermPlan<BITS>::table.s[I];
+    static_assert(s.o >= 0 && s.o + BITS <= 11, "the code stays below bit 11 of its half");
+    constexpr uint32_t mask = (m << s.o) | (m << (16 + s.o));
+    return __builtin_amdgcn_perm(stream_word<BITS, s.q0>(w), stream_word<BITS, s.q1>(w), s.sel) &
+           mask;
+  }
+}
+
+// Slots visited by offset, highest first, so that one accumulator serves all
+// of them: before the slots of a lower offset the running sum is scaled by
+// the (exact) power of two between the two offsets, which keeps it equal to
+// sum x*q * 2^(o-24) at the current offset o (Horner).
+struct SlotOrder {
+  int idx[32];
+  int n;
 };
 
-template <int BITS, int I = 0>
-__device__ __forceinline__ void f16_sub_slots(const uint32_t* w, const uint32_t* xs,
-                                              float (&acc)[F16SubPlan<BITS>::noff]) {
-  if constexpr (I < F16Plan<BITS>::n) {
-    constexpr PairSlot s = F16Plan<BITS>::table.s[I];
-    static_assert(s.klo < 0 || s.khi < 0 || s.olo == s.ohi, "paired codes share their offset");
-    uint32_t win;
-    if constexpr (s.shift == 0) {
-      win = w[s.word];
-    } else if constexpr (s.word + 1 < BITS) {
-      win = __builtin_amdgcn_alignbit(w[s.word + 1], w[s.word], s.shift);
+template <int BITS>
+constexpr SlotOrder f16_slot_order() {
+  SlotOrder ord{};
+  ord.n = F16Slots<BITS>::n;
+  int off[32] = {};
+  for (int i = 0; i < ord.n; ++i) {
+    if constexpr (16 % BITS == 0) {
+      const PairSlot s = F16Slots<BITS>::Plan::table.s[i];
+      off[i] = s.klo >= 0 ? s.olo : s.ohi;
     } else {
-      win = w[s.word] >> s.shift;
+      off[i] = F16PermPlan<BITS>::table.s[i].o;
     }
-    constexpr uint32_t m = (1u << BITS) - 1u;
-    constexpr uint32_t mask = (s.klo >= 0 ? (m << s.olo) : 0u) |
-                              (s.khi >= 0 ? (m << (16 + s.ohi)) : 0u);
-    constexpr int o = s.klo >= 0 ? s.olo : s.ohi;
-    static_assert(o % BITS == 0 && o / BITS < F16SubPlan<BITS>::noff, "offset on the code grid");
-    acc[o / BITS] = dot2<ACT_F16>(xs[I], win & mask, acc[o / BITS]);
-    f16_sub_slots<BITS, I + 1>(w, xs, acc);
+  }
+  int j = 0;
+  for (int o = 10; o >= 0; --o)
+    for (int i = 0; i < ord.n; ++i)
+      if (off[i] == o) ord.idx[j++] = i;
+  return ord;
+}
+
+template <int BITS, int J>
+__device__ __forceinline__ float f16_chain(const uint32_t* w, const uint32_t* xs, float t) {
+  constexpr SlotOrder ord = f16_slot_order<BITS>();
+  if constexpr (J < ord.n) {
+    constexpr int I = ord.idx[J];
+    constexpr int o = f16_slot_offset<BITS, I>();
+    if constexpr (J > 0) {
+      constexpr int prev = f16_slot_offset<BITS, ord.idx[J - 1]>();
+      if constexpr (prev != o) t *= 1.0f / static_cast<float>(1u << (prev - o));
+    }
+    t = dot2<ACT_F16>(xs[I], f16_slot_word<BITS, I>(w), t);
+    return f16_chain<BITS, J + 1>(w, xs, t);
+  } else {
+    return t;
   }
 }
 
+// sum_k x_k q_k over one fp16 run: the chain ends at the lowest offset o_min,
+// in units of 2^(o_min - 24).
 template <int BITS>
-__device__ __forceinline__ float f16_sub_dot(const uint32_t* w, const uint32_t* xs) {
-  constexpr int N = F16SubPlan<BITS>::noff;
-  float acc[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  f16_sub_slots<BITS>(w, xs, acc);
-  // sum_i acc_i * 2^(24 - i*b) = 2^24 * (acc_0 + 2^-b * (acc_1 + 2^-b * (...)))
-  float t = acc[N - 1];
-#pragma unroll
-  for (int i = N - 2; i >= 0; --i) t = __builtin_fmaf(t, 1.0f / static_cast<float>(1u << BITS), acc[i]);
-  return t * 16777216.0f;   // 2^24
+__device__ __forceinline__ float f16_run_dot(const uint32_t* w, const uint32_t* xs) {
+  constexpr SlotOrder ord = f16_slot_order<BITS>();
+  constexpr int lowest = f16_slot_offset<BITS, ord.idx[ord.n - 1]>();
+  return f16_chain<BITS, 0>(w, xs, 0.0f) * static_cast<float>(1u << (24 - lowest));
 }
 
 // Codes 2I and 2I+1 of a run as two exact bf16 values (low half: code 2I).
@@ -218,8 +244,7 @@ __device__ __forceinline__ float f32_dot(const uint32_t* w, const uint32_t* xs, 
 template <int ACT, int BITS>
 __device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) {
   if constexpr (ACT == ACT_F16) {
-    if constexpr (F16SubPlan<BITS>::on) return f16_sub_dot<BITS>(w, xs);
-    else return f16_dot_slots<BITS>(w, xs, 0.0f);
+    return f16_run_dot<BITS>(w, xs);
   } else if constexpr (ACT == ACT_BF16) {
     return bf16_dot_pairs<BITS>(w, xs, 0.0f);
   } else {
