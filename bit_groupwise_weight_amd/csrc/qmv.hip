@@ -55,6 +55,20 @@ template <int BITS> struct F16Slots<BITS, true> {
   static constexpr int khi(int i) { return Plan::table.s[i].khi; }
 };
 
+// Units of the per-row sums until the store: fp16 runs keep their products
+// in the units of the subnormal codes, 2^-24 (x * q * 2^-24 exactly), so the
+// run sums P and X are both taken in those units (X from dot2 with the
+// smallest fp16 subnormal, 2^-24, as the weight of each activation) and the
+// row sum is scaled by 2^24 once, at the store.  bf16 and fp32: units of 1.
+template <int ACT> struct SumUnit {
+  static constexpr uint32_t xweight = Magic<ACT>::ones;   // (unused for fp32)
+  static constexpr float to_one = 1.0f;
+};
+template <> struct SumUnit<ACT_F16> {
+  static constexpr uint32_t xweight = 0x00010001u;        // 2^-24 in each half
+  static constexpr float to_one = 16777216.0f;            // 2^24
+};
+
 // Raw activation words per 32-code run and staged words per run.
 template <int ACT> struct RawWords { static constexpr int n = (ACT == ACT_F32) ? 32 : 16; };
 template <int ACT, int BITS> struct StagedWords;
@@ -90,7 +104,7 @@ __device__ __forceinline__ void stage_run(const uint32_t* raw, uint32_t* out) {
     for (int i = 0; i < 32; ++i) { out[i] = raw[i]; X += __uint_as_float(raw[i]); }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) X = dot2<ACT>(raw[i], Magic<ACT>::ones, X);
+    for (int i = 0; i < 16; ++i) X = dot2<ACT>(raw[i], SumUnit<ACT>::xweight, X);
     if constexpr (ACT == ACT_F16) {
       f16_stage_slots<BITS>(raw, out);
     } else {
@@ -194,13 +208,13 @@ __device__ __forceinline__ float f16_chain(const uint32_t* w, const uint32_t* xs
   }
 }
 
-// sum_k x_k q_k over one fp16 run: the chain ends at the lowest offset o_min,
-// in units of 2^(o_min - 24).
+// sum_k x_k q_k * 2^-24 over one fp16 run: the chain ends at the lowest
+// offset, which every plan has at 0.
 template <int BITS>
 __device__ __forceinline__ float f16_run_dot(const uint32_t* w, const uint32_t* xs) {
   constexpr SlotOrder ord = f16_slot_order<BITS>();
-  constexpr int lowest = f16_slot_offset<BITS, ord.idx[ord.n - 1]>();
-  return f16_chain<BITS, 0>(w, xs, 0.0f) * static_cast<float>(1u << (24 - lowest));
+  static_assert(f16_slot_offset<BITS, ord.idx[ord.n - 1]>() == 0, "chain ends at offset 0");
+  return f16_chain<BITS, 0>(w, xs, 0.0f);
 }
 
 // Codes 2I and 2I+1 of a run as two exact bf16 values (low half: code 2I).
@@ -240,7 +254,8 @@ __device__ __forceinline__ float f32_dot(const uint32_t* w, const uint32_t* xs, 
   }
 }
 
-// sum_k x_k q_k over one run, from the staged words and the run's code words.
+// sum_k x_k q_k over one run (in SumUnit<ACT> units), from the staged words
+// and the run's code words.
 template <int ACT, int BITS>
 __device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) {
   if constexpr (ACT == ACT_F16) {
@@ -360,14 +375,11 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
     __builtin_amdgcn_sched_barrier(0);
 
     // -- weights, scales and zeros of this lane's four runs (addresses
-    // clamped to the matrix; rows past N and runs past K get zero scale and
-    // zero).  Scales and zeros stay raw bits until first use, so these loads
-    // never force an early wait.
+    // clamped to the matrix: a run past K reads the row's last run, a row
+    // past N the last row).  Scales and zeros stay raw bits until first use,
+    // so these loads never force an early wait.
     uint32_t d[R][4 * BITS];
     uint32_t sb[R][4], zb[R][4];
-    bool rok[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rok[j] = rbase + lane + lanes * j < runs;
     using T = typename Act<ACT>::bits_t;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -408,8 +420,9 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
     }
     __syncthreads();
 
-    // -- compute (runs past K and rows past M hold zero activations, and
-    // clamped rows/runs have zero scale and zero, so they add nothing)
+    // -- compute.  Runs past K have zero staged activations and X = 0, so
+    // their clamped copies add s * 0 + z * 0 = 0; rows past N are never
+    // stored; activation rows past M are zero and never stored.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -424,9 +437,8 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float dq = run_dot<ACT, BITS>(&d[r][j * BITS], xs);
-          const bool ok = rok[j] && n_base + r < p.N;
-          const float sv = ok ? act_bits_to_float<ACT>(sb[r][j]) : 0.0f;
-          const float zv = ok ? act_bits_to_float<ACT>(zb[r][j]) : 0.0f;
+          const float sv = act_bits_to_float<ACT>(sb[r][j]);
+          const float zv = act_bits_to_float<ACT>(zb[r][j]);
           acc[r][m] = __builtin_fmaf(sv, dq, acc[r][m]);
           acc[r][m] = __builtin_fmaf(zv, X, acc[r][m]);
         }
@@ -460,7 +472,8 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m >= mcount) break;
-        store_act<ACT>(p.y, static_cast<int64_t>(m0 + m) * p.N + n, acc[r][m] + b);
+        store_act<ACT>(p.y, static_cast<int64_t>(m0 + m) * p.N + n,
+                        __builtin_fmaf(acc[r][m], SumUnit<ACT>::to_one, b));
       }
     }
   }
