@@ -52,6 +52,11 @@ enum QmvVariant { QMV_DEFAULT = 0, QMV_LEAN = 1, QMV_LEAN2 = 2, QMV_LEAN1 = 3 };
 constexpr int qmv_rows_per_group(int bits, int mt, int variant) {
   return mt == 1 && variant != QMV_LEAN1 && (variant == QMV_LEAN2 || bits <= 3) ? 2 : 1;
 }
+// LDS quads (16 bytes) per lane of a row group that the decode kernel stages
+// for `mt` activation rows of `qd` quads per run (four runs per lane): rounded
+// up to an odd count, so that the 16 lanes of one 16-byte LDS read, each at
+// the same quad of its own runs, start in 16 distinct 4-bank groups.
+constexpr int qmv_stage_quads_per_lane(int mt, int qd) { return (mt * 4 * qd) | 1; }
 // Up to kQmvMaxProblems decode problems of one bit width, group size and
 // activation dtype served by one launch: blocks with blockIdx.z == i work on
 // problem i (grid.x is sized for the largest; blocks past a problem's rows

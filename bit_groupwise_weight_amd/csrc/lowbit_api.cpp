@@ -207,11 +207,17 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   }
 
   // Activation rows per pass: as many as fit the LDS stage (at most 4).
+  // max_per_row holds 4 * quads-per-run * 16 bytes per lane, times the lanes.
+  auto stage_bytes = [&](int mt) {
+    const int64_t qd = (max_per_row >> max_shift) / (4 * 16);
+    return static_cast<int64_t>(lowbit::qmv_stage_quads_per_lane(mt, static_cast<int>(qd))) * 16
+           << max_shift;
+  };
   lowbit::QmvLaunch l{};
   l.mt = 1;
-  if (M >= 2 && 2 * max_per_row <= kQmvStageBudget) l.mt = 2;
-  if (M >= 3 && 4 * max_per_row <= kQmvStageBudget) l.mt = 4;
-  if (max_per_row > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
+  if (M >= 2 && stage_bytes(2) <= kQmvStageBudget) l.mt = 2;
+  if (M >= 3 && stage_bytes(4) <= kQmvStageBudget) l.mt = 4;
+  if (stage_bytes(1) > kQmvStageBudget) return fail(LOWBIT_ERR_UNSUPPORTED, "activation stage too large");
   // Block size: 256 threads unless that leaves fewer blocks than CUs.
   int threads = tuning(LOWBIT_TUNE_QMV_BLOCK, 0);
   auto blocks_for = [&](int t, int i, int variant) {

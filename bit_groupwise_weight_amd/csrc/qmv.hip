@@ -323,6 +323,7 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
   constexpr int RAW = RawWords<ACT>::n;
   constexpr int QD = RunQuads<ACT, BITS>::n;    // staged quads per run
   constexpr int GSHIFT = GROUP == 32 ? 5 : GROUP == 64 ? 6 : GROUP == 128 ? 7 : 8;
+  constexpr int SQ = qmv_stage_quads_per_lane(MT, QD);   // LDS quads per lane in a group
 
   const int tid = threadIdx.x;
   const int lanes = 1 << p.lpr_shift;
@@ -359,13 +360,8 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
       const bool valid = rr < nruns && m < mcount && k < p.K;
       // (threads without a real run load nothing: at one activation row
       // they are half the block, and their loads would add half again to the
-      // block's activation traffic)
-      if (valid) {
-        load_raw_run<ACT>(p.x, static_cast<int64_t>(m0 + m) * p.K + k, raw);
-      } else {
-#pragma unroll
-        for (int i = 0; i < RAW; ++i) raw[i] = 0u;
-      }
+      // block's activation traffic; an invalid run stages zeros)
+      if (valid) load_raw_run<ACT>(p.x, static_cast<int64_t>(m0 + m) * p.K + k, raw);
       return valid;
     };
     uint32_t raw[RAW];
@@ -381,37 +377,46 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
     uint32_t d[R][4 * BITS];
     uint32_t sb[R][4], zb[R][4];
     using T = typename Act<ACT>::bits_t;
+    // (run and group indices are unsigned 32-bit, so each address is one
+    // 64-bit add of a zero-extended offset to a per-row base)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int nc = min(n_base + r, p.N - 1);
       const uint8_t* rowp = p.packed + static_cast<int64_t>(nc) * p.row_bytes;
-      const int64_t ro = static_cast<int64_t>(nc) * p.groups;
+      const T* srow = static_cast<const T*>(p.scales) + static_cast<int64_t>(nc) * p.groups;
+      const T* zrow = static_cast<const T*>(p.zeros) + static_cast<int64_t>(nc) * p.groups;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int run = min(rbase + lane + lanes * j, runs - 1);
-        load_run<BITS>(rowp + static_cast<int64_t>(run) * 4 * BITS, &d[r][j * BITS]);
-        const int64_t gi = ro + ((run * 32) >> GSHIFT);
-        sb[r][j] = static_cast<const T*>(p.scales)[gi];
-        zb[r][j] = static_cast<const T*>(p.zeros)[gi];
+        const uint32_t run = static_cast<uint32_t>(min(rbase + lane + lanes * j, runs - 1));
+        load_run<BITS>(rowp + run * (4u * BITS), &d[r][j * BITS]);
+        const uint32_t gi = run >> (GSHIFT - 5);
+        sb[r][j] = srow[gi];
+        zb[r][j] = zrow[gi];
       }
     }
 
-    // -- stage the round's activations: layout [m][j][quad][lane-in-group].
-    // The thread's first run (loaded above, before the weights) is staged
-    // outside the loop so that only the activation loads must have landed.
-    // Threads without a run (past nruns: at one activation row, half the
-    // block) skip the staging arithmetic; runs past M or K stage zeros.
+    // -- stage the round's activations: layout [lane-in-group][m][j][quad],
+    // SQ quads per lane (an odd count, so that 16 lanes reading the same
+    // quad of their own runs hit 16 distinct 4-bank groups), which makes every
+    // read offset below a constant.  The thread's first run (loaded above,
+    // before the weights) is staged outside the loop so that only the
+    // activation loads must have landed.  Threads without a run (past nruns:
+    // at one activation row, half the block) skip the staging arithmetic;
+    // runs past M or K stage zeros.
     auto stage_store = [&](int rr, bool valid) {
       int m, ul, j;
       run_coords(rr, m, ul, j);
+      uint4* dst = stage + ul * SQ + (m * 4 + j) * QD;
+      if (valid) {
+        uint32_t out[QD * 4];
+        stage_run<ACT, BITS>(raw, out);
 #pragma unroll
-      for (int i = 0; i < RAW; ++i) raw[i] = valid ? raw[i] : 0u;
-      uint32_t out[QD * 4];
-      stage_run<ACT, BITS>(raw, out);
+        for (int q = 0; q < QD; ++q)
+          dst[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+      } else {
 #pragma unroll
-      for (int q = 0; q < QD; ++q)
-        stage[((m * 4 + j) * QD + q) * lanes + ul] =
-            make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+        for (int q = 0; q < QD; ++q) dst[q] = make_uint4(0u, 0u, 0u, 0u);
+      }
     };
     if (tid < nruns) stage_store(tid, raw_valid);
     for (int rr = tid + blockDim.x; rr < nruns; rr += blockDim.x) {
@@ -430,7 +435,7 @@ __device__ __forceinline__ void qmv_block(const QmvParams& p, const int bx, uint
         uint32_t xs[QD * 4];
 #pragma unroll
         for (int q = 0; q < QD; ++q) {
-          const uint4 v = stage[((m * 4 + j) * QD + q) * lanes + lane];
+          const uint4 v = stage[lane * SQ + (m * 4 + j) * QD + q];
           xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
         }
         const float X = __uint_as_float(xs[StagedWords<ACT, BITS>::n]);
@@ -502,7 +507,8 @@ static hipError_t launch_one(const QmvBatch& b, const QmvLaunch& l, hipStream_t 
   // staged runs (sized for the widest lane group)
   int shift = 0;
   for (unsigned i = 0; i < l.grid.z; ++i) shift = b.prob[i].lpr_shift > shift ? b.prob[i].lpr_shift : shift;
-  const size_t lds = static_cast<size_t>(MT) * 4 * (size_t(1) << shift) * RunQuads<ACT, LOWBIT_BITS>::n * 16;
+  const size_t lds = (size_t(1) << shift) *
+                    qmv_stage_quads_per_lane(MT, RunQuads<ACT, LOWBIT_BITS>::n) * 16;
   if (l.grid.z == 1)
     qmv_kernel<LOWBIT_BITS, GROUP, ACT, MT, VAR><<<l.grid, l.block, lds, s>>>(b.prob[0]);
   else
