@@ -252,16 +252,20 @@ lowbit_status run_qmv_multi(const QmvProblem* probs, int count, lowbit_dtype act
   bool multi_round = false;
   for (int i = 0; i < count; ++i)
     multi_round |= probs[i].K > (int64_t{128} << b.prob[i].lpr_shift);
-  // Launches too small to give every CU two waves (e.g. N = 1024 at 1-3
-  // bits, two rows per lane group: one wave per CU) take one row per lane
-  // group, which doubles the waves (A/B on one box: K = 4096, N = 1024, b = 1,
-  // 2, 3: 3.81/3.96/4.09 -> 3.59/3.67/3.77 us; K = 2048, N = 1024, b = 1, 3:
-  // 3.12/3.47 -> 2.71/3.10 us; at two waves per CU, N = 2048, it loses 3-4 %).
+  // Otherwise (one round, at most two blocks per CU), widths with two rows
+  // per lane group take one row per lane group, which doubles the waves,
+  // unless that leaves the CUs between two and four waves each.  A/B on one
+  // box, us: K = 4096, N = 1024, b = 1, 2, 3: 3.81/3.96/4.09 -> 3.59/3.67/3.77
+  // and K = 2048, N = 1024, b = 1, 3: 3.12/3.47 -> 2.71/3.10 (one wave per CU
+  // before); K = N = 4096, b = 1, 3: 3.74/4.31 -> 3.67/4.22 and K = 4096,
+  // N = 8192, b = 2, 3: 5.07/5.77 -> 4.92/5.37 (four and eight waves per CU
+  // before); K = 4096, N = 2048 (two waves per CU before) loses 3 %.
   l.variant = lowbit::QMV_DEFAULT;
   const int64_t waves = total_blocks(threads, lowbit::QMV_DEFAULT) * by * (threads / 64);
   if (l.mt == 1 && (total_blocks(threads, lowbit::QMV_DEFAULT) * by > 2 * cus || multi_round))
     l.variant = total_blocks(threads, lowbit::QMV_LEAN2) * by >= 6 * cus ? lowbit::QMV_LEAN2 : lowbit::QMV_LEAN;
-  else if (l.mt == 1 && waves < 2 * cus && lowbit::qmv_rows_per_group(bits, 1, lowbit::QMV_DEFAULT) == 2)
+  else if (l.mt == 1 && (waves < 2 * cus || waves >= 4 * cus) &&
+           lowbit::qmv_rows_per_group(bits, 1, lowbit::QMV_DEFAULT) == 2)
     l.variant = lowbit::QMV_LEAN1;
   const int var_env = tuning(LOWBIT_TUNE_QMV_VARIANT, 0) - 1;   // (override: 1..4 forces variant 0..3)
   if (l.mt == 1 && var_env >= 0 && var_env <= 3) l.variant = var_env;
