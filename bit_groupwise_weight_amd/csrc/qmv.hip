@@ -37,24 +37,6 @@
 
 namespace lowbit {
 
-// The fp16 slot plan of a width (qmv_plan.h): funnel-shift windows for the
-// widths dividing 16 (at 1 bit, windows of 4 bits: four offsets to combine
-// instead of ten), byte permutes for the others.
-template <int BITS, bool PERM = (16 % BITS != 0)> struct F16Slots;
-template <int BITS> struct F16Slots<BITS, false> {
-  static constexpr int span = BITS == 1 ? 4 : f16_default_span<BITS>();
-  using Plan = F16Plan<BITS, span>;
-  static constexpr int n = Plan::n;
-  static constexpr int klo(int i) { return Plan::table.s[i].klo; }
-  static constexpr int khi(int i) { return Plan::table.s[i].khi; }
-};
-template <int BITS> struct F16Slots<BITS, true> {
-  using Plan = F16PermPlan<BITS>;
-  static constexpr int n = Plan::n;
-  static constexpr int klo(int i) { return Plan::table.s[i].klo; }
-  static constexpr int khi(int i) { return Plan::table.s[i].khi; }
-};
-
 // Units of the per-row sums until the store: fp16 runs keep their products
 // in the units of the subnormal codes, 2^-24 (x * q * 2^-24 exactly), so the
 // run sums P and X are both taken in those units (X from dot2 with the
@@ -130,17 +112,15 @@ __device__ __forceinline__ uint32_t stream_word(const uint32_t* w) {
 }
 
 // fp16: slot I of the plan (qmv_plan.h) as one word holding its two codes
-// at bit offset f16_slot_offset(I) of their halves, every other bit clear:
-// the halves read as the fp16 subnormals q * 2^(o-24).
+// at bit offset F16Slots<BITS>::offset(I) of their halves, every other bit
+// clear: the halves read as the fp16 subnormals q * 2^(o-24).
 template <int BITS, int I>
 constexpr int f16_slot_offset() {
   if constexpr (16 % BITS == 0) {
     constexpr PairSlot s = F16Slots<BITS>::Plan::table.s[I];
     static_assert(s.klo < 0 || s.khi < 0 || s.olo == s.ohi, "paired codes share their offset");
-    return s.klo >= 0 ? s.olo : s.ohi;
-  } else {
-    return F16PermPlan<BITS>::table.s[I].o;
   }
+  return F16Slots<BITS>::offset(I);
 }
 
 template <int BITS, int I>
@@ -175,19 +155,10 @@ template <int BITS>
 constexpr SlotOrder f16_slot_order() {
   SlotOrder ord{};
   ord.n = F16Slots<BITS>::n;
-  int off[32] = {};
-  for (int i = 0; i < ord.n; ++i) {
-    if constexpr (16 % BITS == 0) {
-      const PairSlot s = F16Slots<BITS>::Plan::table.s[i];
-      off[i] = s.klo >= 0 ? s.olo : s.ohi;
-    } else {
-      off[i] = F16PermPlan<BITS>::table.s[i].o;
-    }
-  }
   int j = 0;
   for (int o = 10; o >= 0; --o)
     for (int i = 0; i < ord.n; ++i)
-      if (off[i] == o) ord.idx[j++] = i;
+      if (F16Slots<BITS>::offset(i) == o) ord.idx[j++] = i;
   return ord;
 }
 
