@@ -167,12 +167,13 @@ struct F16PermPlan {
 // ---------------------------------------------------- plan of a width --
 
 // The fp16 slot plan of a width: funnel-shift windows for the widths dividing
-// 16 (at 1 bit, windows of 4 bits: four offsets to combine instead of ten),
-// byte permutes for the others.  klo/khi: the codes of slot i; offset: their
+// 16 (at 1 bit, windows of 4 bits: four offsets to combine instead of ten; at
+// 2 bits, of 8: four offsets instead of five, same shifts), byte permutes for
+// the others.  klo/khi: the codes of slot i; offset: their
 // common bit offset.
 template <int BITS, bool PERM = (16 % BITS != 0)> struct F16Slots;
 template <int BITS> struct F16Slots<BITS, false> {
-  static constexpr int span = BITS == 1 ? 4 : f16_default_span<BITS>();
+  static constexpr int span = BITS == 1 ? 4 : BITS == 2 ? 8 : f16_default_span<BITS>();
   using Plan = F16Plan<BITS, span>;
   static constexpr int n = Plan::n;
   static constexpr int klo(int i) { return Plan::table.s[i].klo; }
