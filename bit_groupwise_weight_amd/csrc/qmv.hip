@@ -64,14 +64,19 @@ template <int ACT, int BITS> struct RunQuads {
 
 // ---------------------------------------------------------------- staging --
 
+// Slot I's activation pair: x[klo] in the low half, x[khi] in the high half,
+// gathered from the raw pairs (x[2i], x[2i+1]) with one byte permute (a
+// missing code's half selects zero bytes).
 template <int BITS, int I = 0>
 __device__ __forceinline__ void f16_stage_slots(const uint32_t* raw, uint32_t* out) {
   if constexpr (I < F16Slots<BITS>::n) {
     constexpr int klo = F16Slots<BITS>::klo(I), khi = F16Slots<BITS>::khi(I);
-    uint32_t lo = 0, hi = 0;
-    if constexpr (klo >= 0) lo = (raw[klo >> 1] >> ((klo & 1) * 16)) & 0xffffu;
-    if constexpr (khi >= 0) hi = (raw[khi >> 1] >> ((khi & 1) * 16)) & 0xffffu;
-    out[I] = lo | (hi << 16);
+    constexpr uint32_t kZero = 0x0cu;   // v_perm_b32 selector of a zero byte
+    constexpr uint32_t lo0 = klo >= 0 ? (klo & 1) * 2u : kZero;       // bytes of S1
+    constexpr uint32_t hi0 = khi >= 0 ? 4u + (khi & 1) * 2u : kZero;  // bytes of S0
+    constexpr uint32_t sel = lo0 | ((klo >= 0 ? lo0 + 1 : kZero) << 8) | (hi0 << 16) |
+                             ((khi >= 0 ? hi0 + 1 : kZero) << 24);
+    out[I] = __builtin_amdgcn_perm(raw[(khi >= 0 ? khi : 0) >> 1], raw[(klo >= 0 ? klo : 0) >> 1], sel);
     f16_stage_slots<BITS, I + 1>(raw, out);
   }
 }
