@@ -188,6 +188,19 @@ def test_qmv_small(bits, act):
         run_small_linear(M, N, K, bits, group, act, bias, lb.PATH_QMV, seed=bits + M + K)
 
 
+@pytest.mark.parametrize("act", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("bits", range(1, 8))
+def test_qmv_long_rows(bits, act):
+    """Rows longer than 64 lanes of four 32-code runs (K > 8192), which the
+    decode kernel takes in several rounds: K just past 8192 and 14336 (a
+    ragged second round), 16384 (two exact rounds), just past 16384 (a third
+    round of one run per lane group); one and two activation rows."""
+    for (M, N, K, group, bias) in [(1, 37, 8224, 32, True), (1, 70, 14336, 64, False),
+                                   (1, 33, 16384, 256, True), (1, 20, 16416, 32, False),
+                                   (2, 24, 14336, 128, True)]:
+        run_small_linear(M, N, K, bits, group, act, bias, lb.PATH_QMV, seed=bits + M + K)
+
+
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", range(1, 8))
 def test_qmm_small(bits, act):
