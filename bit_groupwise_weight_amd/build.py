@@ -110,7 +110,35 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
         os.replace(tmp, lib)
+    build_fastcall()
     return LIB_PATH
+
+
+FASTCALL_SRC = os.path.join(PKG, "_fastcall.c")
+
+
+def fastcall_path() -> str:
+    import sysconfig
+    return os.path.join(PKG, "_lowbit_fastcall" + (sysconfig.get_config_var("EXT_SUFFIX") or ".so"))
+
+
+def build_fastcall() -> str | None:
+    """The binding's argument-marshalling module for eager calls (plain C
+    against the Python headers; the binding uses ctypes without it)."""
+    import sysconfig
+    cc = shutil.which("gcc") or shutil.which("cc")
+    inc = sysconfig.get_paths().get("include")
+    if cc is None or inc is None or not os.path.exists(os.path.join(inc, "Python.h")):
+        return None
+    out = fastcall_path()
+    tmp = out + ".tmp"
+    cmd = [cc, "-O2", "-Wall", "-Wextra", "-shared", "-fPIC", "-I", inc, "-I", INCLUDE,
+           FASTCALL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"fastcall module build failed:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

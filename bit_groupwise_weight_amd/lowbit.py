@@ -316,6 +316,16 @@ def lowbit_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, z
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
+def _fastcall_module():
+    """The compiled argument-marshalling module for eager calls, or None
+    (then PreparedLinear passes ctypes values; both call the same entry)."""
+    try:
+        from bit_groupwise_weight_amd import _lowbit_fastcall
+        return _lowbit_fastcall
+    except ImportError:
+        return None
+
+
 class PreparedLinear:
     """One layer's weights bound to lowbit_linear once, for eager calls.
 
@@ -328,7 +338,7 @@ class PreparedLinear:
     """
 
     __slots__ = ("N", "K", "bits", "group", "dtype", "act", "device", "dev_index", "_ptrs",
-                 "_keep", "_fn", "_ws", "_const", "_one_device")
+                 "_keep", "_fn", "_ws", "_const", "_one_device", "_fc", "_bound")
 
     def __init__(self, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                  bias: Optional[torch.Tensor], bits: int, group: int):
@@ -357,6 +367,14 @@ class PreparedLinear:
         vp, ci = ctypes.c_void_p, ctypes.c_int
         self._const = (ci(self.act), vp(self._ptrs[0]), vp(self._ptrs[1]), vp(self._ptrs[2]),
                        vp(self._ptrs[3]), ci(bits), ci(group), ctypes.c_int64(N), ctypes.c_int64(K))
+        # with the compiled marshalling module, the fixed arguments are bound
+        # once in C and a call passes seven ints
+        self._fc = _fastcall_module()
+        self._bound = None
+        if self._fc is not None:
+            fn = ctypes.cast(lib.lowbit_linear, ctypes.c_void_p).value
+            self._bound = self._fc.bind(fn, self.act, self._ptrs[0], self._ptrs[1], self._ptrs[2],
+                                        self._ptrs[3], bits, group, N, K)
         self._ws = {}
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -382,18 +400,23 @@ class PreparedLinear:
         if tail is None:
             need = load().lowbit_linear_workspace_bytes(self.bits, self.group, M, N, self.K, self.act)
             buf = cached_workspace(self.device, s, need) if M > 0 else None
-            ws_ptr, ws_bytes = (None, 0) if buf is None else (buf.data_ptr(), buf.numel())
-            tail = (ctypes.c_int64(M), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(s))
+            ws_ptr, ws_bytes = (0, 0) if buf is None else (buf.data_ptr(), buf.numel())
+            tail = (ws_ptr, ws_bytes, ctypes.c_int64(M), ctypes.c_void_p(ws_ptr or None),
+                    ctypes.c_size_t(ws_bytes), ctypes.c_void_p(s))
             self._ws[key] = tail
-        act, pk, sp, zp, bp, bits, group, n, k = self._const
-        m, wp, wb, sh = tail
-        args = (ctypes.c_void_p(x.data_ptr()), act, pk, sp, zp, bp, ctypes.c_void_p(y.data_ptr()),
-                bits, group, m, n, k, wp, wb, sh)
-        if self._one_device or torch.cuda.current_device() == self.dev_index:
-            st = self._fn(*args)
+        same_device = self._one_device or torch.cuda.current_device() == self.dev_index
+        if self._bound is not None and same_device:
+            st = self._fc.call(self._bound, x.data_ptr(), y.data_ptr(), M, tail[0], tail[1], s)
         else:
-            with torch.cuda.device(self.device):
+            act, pk, sp, zp, bp, bits, group, n, k = self._const
+            m, wp, wb, sh = tail[2:]
+            args = (ctypes.c_void_p(x.data_ptr()), act, pk, sp, zp, bp, ctypes.c_void_p(y.data_ptr()),
+                    bits, group, m, n, k, wp, wb, sh)
+            if same_device:
                 st = self._fn(*args)
+            else:
+                with torch.cuda.device(self.device):
+                    st = self._fn(*args)
         if st != LOWBIT_OK:
             _check(st, "lowbit_linear")
         return y

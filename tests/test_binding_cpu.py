@@ -114,3 +114,44 @@ def test_prepared_linear_checks_weights_once_at_construction():
         lb.PreparedLinear(packed, scales, zeros.to(torch.bfloat16), None, BITS, GROUP)
     with pytest.raises(ValueError, match="GPU memory"):
         lb.PreparedLinear(packed, scales, zeros, None, BITS, GROUP)
+
+
+@pytest.mark.parametrize("case", [
+    dict(bits=8), dict(group=48), dict(M=0), dict(M=-1), dict(x=0), dict(x=0x10004),
+    dict(packed=0x10008), dict(ws=0, ws_bytes=64), dict(act=7), dict(N=0), dict(K=96),
+    dict(bias=0x10000, M=0)])
+def test_fastcall_passes_arguments_unchanged(case):
+    """The compiled marshalling module of PreparedLinear hands lowbit_linear
+    the same arguments as ctypes: on calls the library settles before any
+    HIP call (argument errors, M = 0), status and message agree."""
+    import ctypes
+    fc = lb._fastcall_module()
+    if fc is None:
+        pytest.skip("the marshalling module is not built")
+    lib = lb.load()
+    a = dict(x=0x10000, act=1, packed=0x10000, scales=0x10000, zeros=0x10000, bias=None,
+             y=0x10000, bits=4, group=64, M=1, N=64, K=256, ws=0, ws_bytes=0)
+    a.update(case)
+    vp = lambda v: ctypes.c_void_p(v or None)
+    st_ct = lib.lowbit_linear(vp(a["x"]), a["act"], vp(a["packed"]), vp(a["scales"]),
+                              vp(a["zeros"]), vp(a["bias"]), vp(a["y"]), a["bits"], a["group"],
+                              ctypes.c_int64(a["M"]), ctypes.c_int64(a["N"]), ctypes.c_int64(a["K"]),
+                              vp(a["ws"]), ctypes.c_size_t(a["ws_bytes"]), None)
+    msg_ct = lb.lowbit_last_error()
+    fn = ctypes.cast(lib.lowbit_linear, ctypes.c_void_p).value
+    bound = fc.bind(fn, a["act"], a["packed"], a["scales"], a["zeros"], a["bias"], a["bits"],
+                    a["group"], a["N"], a["K"])
+    st_fc = fc.call(bound, a["x"], a["y"], a["M"], a["ws"], a["ws_bytes"], 0)
+    assert st_fc == st_ct
+    if st_ct != 0:
+        assert lb.lowbit_last_error() == msg_ct
+
+
+def test_fastcall_rejects_bad_arity():
+    fc = lb._fastcall_module()
+    if fc is None:
+        pytest.skip("the marshalling module is not built")
+    with pytest.raises(TypeError):
+        fc.call(1, 2)
+    with pytest.raises(TypeError):
+        fc.bind(1)
