@@ -230,6 +230,32 @@ __device__ __forceinline__ float f32_dot(const uint32_t* w, const uint32_t* xs, 
   }
 }
 
+// Widths dividing 8: byte planes.  Plane j of a word keeps bits j*b.. of
+// every byte, i.e. code CPB*i + j of the word in byte i (CPB = 8/b codes per
+// byte), so one shift and one AND serve four codes and each code converts with
+// one v_cvt_f32_ubyteN (instead of a field extract and a conversion).
+template <int BITS>
+__device__ __forceinline__ float f32_dot_planes(const uint32_t* w, const uint32_t* xs) {
+  constexpr int CPB = 8 / BITS;
+  constexpr int CPW = 32 / BITS;                   // codes per word
+  constexpr uint32_t m = ((1u << BITS) - 1u) * 0x01010101u;
+  float acc = 0.0f;
+#pragma unroll
+  for (int d = 0; d < BITS; ++d) {
+#pragma unroll
+    for (int j = 0; j < CPB; ++j) {
+      uint32_t plane = (w[d] >> (j * BITS)) & m;
+      asm("" : "+v"(plane));   // (opaque: else the byte reads fold back into field extracts)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = d * CPW + i * CPB + j;
+        acc = __builtin_fmaf(__uint_as_float(xs[k]), static_cast<float>((plane >> (8 * i)) & 0xffu), acc);
+      }
+    }
+  }
+  return acc;
+}
+
 // sum_k x_k q_k over one run (in SumUnit<ACT> units), from the staged words
 // and the run's code words.
 template <int ACT, int BITS>
@@ -238,6 +264,8 @@ __device__ __forceinline__ float run_dot(const uint32_t* w, const uint32_t* xs) 
     return f16_run_dot<BITS>(w, xs);
   } else if constexpr (ACT == ACT_BF16) {
     return bf16_dot_pairs<BITS>(w, xs, 0.0f);
+  } else if constexpr (8 % BITS == 0) {
+    return f32_dot_planes<BITS>(w, xs);
   } else {
     return f32_dot<BITS>(w, xs, 0.0f);
   }
