@@ -45,6 +45,23 @@ Readings where the pages are silent (each one is listed in the design notes):
   R22 signed zeros compare equal in the min/max scan; a zero minimum or maximum
       is taken as +0.
 
+Activation-quantized variant (the "-qmode 8da4w -G 32" export mode of
+"[MPS] Add support for Int4 groupwise quantization": 8-bit dynamic
+activations with 4-bit weights in groups of 32; the page names the mode and
+nothing of its arithmetic, so these readings fix it):
+  R30 each activation row m is quantized on the fly to signed 8-bit codes with
+      one fp32 scale: a_m = max_k |x[m, k]| / 127 (an fp32 correctly rounded
+      divide), xq[m, k] = clamp(rint_half_even(x[m, k] / a_m), -127, 127) with
+      the divide in fp32 (symmetric: no zero point, -128 unused).
+  R31 a row whose a_m is 0 (all zeros, or a maximum so small that the divide
+      underflows) gets all codes 0.
+  R32 a row holding a NaN or an infinity gets a_m = NaN and all codes 0, so
+      its outputs are NaN.
+  R33 the weights keep this module's format (R1-R11, any width and group);
+      y[m, n] = sum_k (a_m * xq[m, k]) * w[n, k] (+ bias[n]): the integer
+      group sums sum xq*q and sum xq are exact, and the tolerance of the
+      weight-only linear applies with x replaced by a_m * xq.
+
 Parity status: every function below is pinned by tests that do not reuse its
 own formula (golden packing vectors derived by hand, a big-integer bit-stream
 formulation, a pure-Python bit reader, exact-grid / tie / constant-group closed
@@ -254,3 +271,40 @@ def linear_rows(x: np.ndarray, q_rows: np.ndarray, s_rows: np.ndarray, z_rows: n
                 group: int, bias_rows: Optional[np.ndarray] = None):
     """linear() restricted to a subset of output rows (for sampled parity at full size)."""
     return linear(x, q_rows, s_rows, z_rows, group, bias_rows)
+
+
+# ----------------------------------------------- dynamic int8 activations --
+
+def quantize_activations_i8(x: np.ndarray):
+    """Per-row symmetric int8 quantization of the activations (R30-R32).
+
+    x: [M, K], values of the activations (fp32, or fp16 / bf16 values, which
+    are fp32 values).  Returns (xq int8 [M, K], a float32 [M]).
+    """
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x32.shape
+    xq = np.zeros((M, K), dtype=np.int8)
+    a = np.zeros(M, dtype=np.float32)
+    for m in range(M):
+        row = x32[m]
+        if not np.all(np.isfinite(row)):
+            a[m] = np.float32(np.nan)                       # R32
+            continue
+        amax = np.max(np.abs(row))                          # exact
+        a[m] = np.float32(amax) / np.float32(127.0)         # fp32 divide
+        if a[m] == 0:
+            continue                                        # R31
+        t = (row / a[m]).astype(np.float32)                 # fp32 divide per element
+        xq[m] = np.clip(np.rint(t), -127, 127).astype(np.int8)   # half to even
+    return xq, a
+
+
+def linear_a8(xq: np.ndarray, a: np.ndarray, q: np.ndarray, s: np.ndarray, z: np.ndarray,
+              group: int, bias: Optional[np.ndarray] = None):
+    """fp64 reference of the linear over int8 activations (R33).
+
+    Returns (y_ref [M, N], A [M, N]) as linear() does, with the activations
+    a_m * xq[m, k] (exact in float64).
+    """
+    xd = np.asarray(a, dtype=np.float64)[:, None] * np.asarray(xq, dtype=np.float64)
+    return linear(xd, q, s, z, group, bias)
