@@ -154,6 +154,38 @@ hipError_t launch_qmm_bf16_b5(const QmmParams&, const QmmLaunch&, hipStream_t);
 hipError_t launch_qmm_bf16_b6(const QmmParams&, const QmmLaunch&, hipStream_t);
 hipError_t launch_qmm_bf16_b7(const QmmParams&, const QmmLaunch&, hipStream_t);
 
+// ------------------------------------------- int8 dynamic activations --
+struct ActQuantParams {
+  const void* x;          // M x K act (fp32, fp16 or bf16), 16-byte aligned
+  int8_t* xq;             // M x K codes, 16-byte aligned
+  float* ascale;          // M
+  int M, K;               // K % 16 == 0
+};
+hipError_t launch_act_quant_i8(const ActQuantParams&, int act, hipStream_t);
+
+struct A8Params {
+  const int8_t* xq;       // M x K codes, 16-byte aligned
+  const float* ascale;    // M
+  const uint8_t* packed;  // N x row_bytes
+  const void* scales;     // N x groups, sz dtype
+  const void* zeros;      // N x groups, sz dtype
+  const void* bias;       // N, sz dtype, or nullptr
+  void* y;                // M x N, sz dtype
+  int M, N, K;
+  int groups;             // K / group
+  int group;
+  int64_t row_bytes;      // K * bits / 8
+};
+// Blocks of 4 waves, one 16-column MFMA tile per wave, `mtt` (1, 2 or 4)
+// 16-row tiles per block: grid (ceil(N / 64), ceil(M / (16 * mtt))).
+hipError_t launch_qmm_a8_b1(const A8Params&, int mtt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b2(const A8Params&, int mtt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b3(const A8Params&, int mtt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b4(const A8Params&, int mtt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b5(const A8Params&, int mtt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b6(const A8Params&, int mtt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b7(const A8Params&, int mtt, int sz, hipStream_t);
+
 // ------------------------------------------------- library-owned scratch --
 // Size of the device array behind lowbit_linear_noalloc (per device).  The
 // largest K-split schedule of the MFMA path writes one fp32 partial per

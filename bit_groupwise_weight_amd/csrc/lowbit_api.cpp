@@ -500,6 +500,33 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   return LOWBIT_OK;
 }
 
+typedef hipError_t (*A8Launcher)(const lowbit::A8Params&, int, int, hipStream_t);
+const A8Launcher kA8[8] = {nullptr,
+                           lowbit::launch_qmm_a8_b1,
+                           lowbit::launch_qmm_a8_b2,
+                           lowbit::launch_qmm_a8_b3,
+                           lowbit::launch_qmm_a8_b4,
+                           lowbit::launch_qmm_a8_b5,
+                           lowbit::launch_qmm_a8_b6,
+                           lowbit::launch_qmm_a8_b7};
+
+// Largest M of the int8-activation linear: 65535 blocks of 16 rows.
+constexpr int64_t kA8MaxM = int64_t(1) << 20;
+
+// 16-row tiles per block of the int8-activation linear: the most (4, 2, 1)
+// that still leaves two waves per SIMD (each wave is one 16-column tile),
+// and no more than the rows need.
+int a8_row_tiles(int64_t M, int64_t N) {
+  const int forced = tuning(LOWBIT_TUNE_A8_MTT, 0);
+  if (forced == 1 || forced == 2 || forced == 4) return forced;
+  const int64_t col_waves = (N + 15) / 16;
+  const int64_t target = int64_t(8) * device_cus();
+  int mtt = 4;
+  while (mtt > 1 && (16 * (mtt / 2) >= M || col_waves * ((M + 16 * mtt - 1) / (16 * mtt)) < target))
+    mtt /= 2;
+  return mtt;
+}
+
 }  // namespace
 
 extern "C" {
@@ -677,6 +704,61 @@ lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lo
   }
   if (count == 0 || M == 0) return LOWBIT_OK;
   return run_qmv_multi(probs, count, act_dtype, bits, group, M, static_cast<hipStream_t>(stream));
+}
+
+lowbit_status lowbit_quantize_act_i8(const void* x, lowbit_dtype act_dtype, int64_t M, int64_t K,
+                                     int8_t* xq, float* ascale, void* stream) {
+  g_last_error.clear();
+  if (!valid_dtype(act_dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "act_dtype=%d", (int)act_dtype);
+  if (M < 0 || M > kMaxDim) return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld", (long long)M);
+  if (K <= 0 || K > kMaxDim || K % 32 != 0)
+    return fail(LOWBIT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 32 (at most 2^30)",
+                (long long)K);
+  if (M == 0) return LOWBIT_OK;
+  if (!x || !xq || !ascale) return fail(LOWBIT_ERR_INVALID_ARG, "NULL x, xq or ascale");
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(ascale, 4))
+    return fail(LOWBIT_ERR_MISALIGNED, "x and xq must be 16-byte aligned, ascale 4-byte aligned");
+  lowbit::ActQuantParams p{x, xq, ascale, static_cast<int>(M), static_cast<int>(K)};
+  const hipError_t e = lowbit::launch_act_quant_i8(p, act_kind(act_dtype), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "act_quant_i8 launch");
+  return LOWBIT_OK;
+}
+
+lowbit_status lowbit_linear_a8(const int8_t* xq, const float* ascale, const uint8_t* packed,
+                               const void* scales, const void* zeros, const void* bias, void* y,
+                               lowbit_dtype dtype, int bits, int group, int64_t M, int64_t N,
+                               int64_t K, void* stream) {
+  g_last_error.clear();
+  lowbit_status st = check_common(bits, group, N, K);
+  if (st != LOWBIT_OK) return st;
+  if (M < 0 || M > kA8MaxM) return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld not in 0..2^20", (long long)M);
+  if (!valid_dtype(dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "dtype=%d", (int)dtype);
+  if (!packed || !scales || !zeros) return fail(LOWBIT_ERR_INVALID_ARG, "NULL weight pointer");
+  if (M == 0) return LOWBIT_OK;
+  if (!xq || !ascale || !y) return fail(LOWBIT_ERR_INVALID_ARG, "NULL xq, ascale or y");
+  if (!aligned(packed, 16) || !aligned(xq, 16))
+    return fail(LOWBIT_ERR_MISALIGNED, "packed and xq must be 16-byte aligned");
+  const size_t e = dtype_bytes(dtype);
+  if (!aligned(ascale, 4) || !aligned(scales, e) || !aligned(zeros, e) || !aligned(y, e) ||
+      (bias && !aligned(bias, e)))
+    return fail(LOWBIT_ERR_MISALIGNED, "ascale/scales/zeros/bias/y must be aligned to their element size");
+  lowbit::A8Params p{};
+  p.xq = xq;
+  p.ascale = ascale;
+  p.packed = packed;
+  p.scales = scales;
+  p.zeros = zeros;
+  p.bias = bias;
+  p.y = y;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.K = static_cast<int>(K);
+  p.groups = static_cast<int>(K / group);
+  p.group = group;
+  p.row_bytes = K * bits / 8;
+  const hipError_t he = kA8[bits](p, a8_row_tiles(M, N), act_kind(dtype), static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "qmm_a8 launch");
+  return LOWBIT_OK;
 }
 
 }  // extern "C"

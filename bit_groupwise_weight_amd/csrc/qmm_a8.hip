@@ -1,0 +1,302 @@
+// Linear over int8 activations (the activation-quantized variant: 8-bit
+// dynamic activations with groupwise low-bit weights, the export mode that
+// "[MPS] Add support for Int4 groupwise quantization" runs with 4-bit weights
+// in groups of 32) on the gfx950 int8 MFMA:
+//
+//   y[m, n] = a_m * sum_g (s[n, g] * P[m, n, g] + z[n, g] * X[m, g]) (+ bias[n])
+//   P = sum over group g of xq * q   (exact in int32)
+//   X = sum over group g of xq       (exact in int32)
+//
+// Both integer sums come from v_mfma_i32_16x16x64_i8: P with the codes as
+// the B operand, X with a ones operand, so X lands in the same lanes as P.
+// Each group's sums are turned into fp32 and scaled once (two fused
+// multiply-adds per output and group), and a_m and the bias enter once at
+// the store, rounded once to the output type.
+//
+// Operand layout: a 64-wide K window per MFMA; lane l supplies row (A) or
+// column (B) l % 16 and the 16 K positions 16 (l / 16) .. 16 (l / 16) + 15
+// of the window, one byte each, in order.  The MFMA pairs byte e of lane
+// group j of A with byte e of lane group j of B, so any fixed assignment of
+// K positions to (lane group, byte) that both operands share gives the same
+// sums; this one lets A be one 16-byte load of a row and B the 2*BITS bytes
+// of 16 consecutive codes.  A group of 32 is half a window: its two groups
+// take two passes whose B (and ones) operands are zero in the other half's
+// lane groups; a row of K = 64 w + 32 ends with a half window, whose missing
+// half the lanes read from the window's first half and mask out.
+//
+// Block: 4 waves, each one 16-column tile over MTT 16-row tiles and all of
+// K; the next window's codes, activations and scales are loaded before the
+// current window is multiplied.  No LDS and no barriers: a wave past N
+// returns at once.
+#include "qmm_common.h"
+
+#ifndef LOWBIT_BITS
+#error "compile with -DLOWBIT_BITS=<1..7>"
+#endif
+
+namespace lowbit {
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t mfma_i8(i32x4_t a, i32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// The words holding one lane's 16 codes (K positions kk .. kk + 15 of a
+// weight row, kk % 16 == 0): 2*BITS bytes from byte kk*BITS/8.  For even
+// BITS they are whole aligned words; for odd BITS they may start in the
+// middle of a word, so one more word is read and the lane shifts by 16 bits.
+// (The extra bytes belong to the next 16 codes of the same row.)
+template <int BITS>
+struct CodeWords {
+  static constexpr int NL = (BITS + 1) / 2;
+  uint32_t w[NL];
+  uint32_t sh;
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_code_words(const uint8_t* row, uint32_t kk,
+                                                CodeWords<BITS>& cw) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  constexpr int NL = CodeWords<BITS>::NL;
+  const uint32_t off = (kk >> 4) * (2 * BITS);
+  const uint8_t* src = static_cast<const uint8_t*>(__builtin_assume_aligned(row + (off & ~3u), 4));
+  if constexpr (NL == 1) {
+    __builtin_memcpy(&cw.w[0], src, 4);
+  } else if constexpr (NL == 2) {
+    u32x2 v;
+    __builtin_memcpy(&v, src, 8);
+    cw.w[0] = v.x; cw.w[1] = v.y;
+  } else if constexpr (NL == 3) {
+    u32x3 v;
+    __builtin_memcpy(&v, src, 12);
+    cw.w[0] = v.x; cw.w[1] = v.y; cw.w[2] = v.z;
+  } else {
+    u32x4 v;
+    __builtin_memcpy(&v, src, 16);
+    cw.w[0] = v.x; cw.w[1] = v.y; cw.w[2] = v.z; cw.w[3] = v.w;
+  }
+  cw.sh = (off & 3u) * 8u;
+}
+
+// The 16 codes as 16 bytes in K order (the B operand).
+template <int BITS>
+__device__ __forceinline__ i32x4_t expand_codes(const CodeWords<BITS>& cw) {
+  constexpr int NL = CodeWords<BITS>::NL;
+  uint32_t S[NL];
+  if constexpr (BITS % 2 == 1) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      S[i] = __builtin_amdgcn_alignbit(i + 1 < NL ? cw.w[i + 1] : 0u, cw.w[i], cw.sh);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) S[i] = cw.w[i];
+  }
+  if constexpr (BITS == 4) {
+    // even codes in the bytes of lo, odd codes in the bytes of hi; two byte
+    // permutes per word put them in order
+    const uint32_t lo0 = and_nibbles(S[0]), hi0 = and_nibbles(S[0] >> 4);
+    const uint32_t lo1 = and_nibbles(S[1]), hi1 = and_nibbles(S[1] >> 4);
+    return i32x4_t{static_cast<int>(__builtin_amdgcn_perm(hi0, lo0, 0x05010400u)),
+                   static_cast<int>(__builtin_amdgcn_perm(hi0, lo0, 0x07030602u)),
+                   static_cast<int>(__builtin_amdgcn_perm(hi1, lo1, 0x05010400u)),
+                   static_cast<int>(__builtin_amdgcn_perm(hi1, lo1, 0x07030602u))};
+  } else {
+    uint32_t d[4];
+    static_for<4>([&](auto dd) {
+      constexpr int D = decltype(dd)::value;
+      d[D] = code_at<BITS, 4 * D>(S) | (code_at<BITS, 4 * D + 1>(S) << 8) |
+             (code_at<BITS, 4 * D + 2>(S) << 16) | (code_at<BITS, 4 * D + 3>(S) << 24);
+    });
+    return i32x4_t{static_cast<int>(d[0]), static_cast<int>(d[1]), static_cast<int>(d[2]),
+                   static_cast<int>(d[3])};
+  }
+}
+
+template <int MTT, int SZ, typename T>
+__device__ __forceinline__ void rescale(float (&acc)[MTT][4], const i32x4_t (&P)[MTT],
+                                        const i32x4_t (&X)[MTT], T sb, T zb) {
+  const float s = act_bits_to_float<SZ>(sb);
+  const float z = act_bits_to_float<SZ>(zb);
+#pragma unroll
+  for (int t = 0; t < MTT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[t][i] = fmaf(s, static_cast<float>(P[t][i]), acc[t][i]);
+      acc[t][i] = fmaf(z, static_cast<float>(X[t][i]), acc[t][i]);
+    }
+  }
+}
+
+template <int BITS, int MTT, bool G32, int SZ>
+__global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
+  using T = typename Act<SZ>::bits_t;
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+  if (n0 >= p.N) return;
+  const int c = lane & 15;
+  const uint32_t j = lane >> 4;
+  const int m0 = blockIdx.y * 16 * MTT;
+  const int nc = min(n0 + c, p.N - 1);
+  const uint8_t* wrow = p.packed + static_cast<size_t>(nc) * p.row_bytes;
+  const T* srow = static_cast<const T*>(p.scales) + static_cast<size_t>(nc) * p.groups;
+  const T* zrow = static_cast<const T*>(p.zeros) + static_cast<size_t>(nc) * p.groups;
+  const int8_t* arow[MTT];
+#pragma unroll
+  for (int t = 0; t < MTT; ++t)
+    arow[t] = p.xq + static_cast<size_t>(min(m0 + 16 * t + c, p.M - 1)) * p.K;
+
+  const uint32_t K = p.K;
+  const int W = static_cast<int>((K + 63) >> 6);
+  const int wg_shift = G32 ? 0 : __builtin_ctz(static_cast<uint32_t>(p.group >> 6));
+  const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  const i32x4_t zero4 = {0, 0, 0, 0};
+
+  // K position of this lane's 16 codes in window w; the missing half of a
+  // final half window reads the window's first half (masked out below)
+  auto lane_k = [&](int w) -> uint32_t {
+    const uint32_t kk = 64u * static_cast<uint32_t>(w) + 16u * j;
+    return kk >= K ? kk - 32u : kk;
+  };
+  // scale/zero index of pass h of window w (G32: group 2w + h, clamped for a
+  // half window; otherwise the window's group)
+  auto sz_index = [&](int w, int h) -> int {
+    return G32 ? min(2 * w + h, p.groups - 1) : (w >> wg_shift);
+  };
+
+  CodeWords<BITS> cw;
+  i32x4_t a[MTT];
+  T sb[2], zb[2];
+  {
+    const uint32_t kk = lane_k(0);
+    load_code_words<BITS>(wrow, kk, cw);
+#pragma unroll
+    for (int t = 0; t < MTT; ++t) a[t] = *reinterpret_cast<const i32x4_t*>(arow[t] + kk);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sb[h] = srow[sz_index(0, h)];
+      zb[h] = zrow[sz_index(0, h)];
+    }
+  }
+
+  float acc[MTT][4];
+  i32x4_t P[MTT], X[MTT];
+#pragma unroll
+  for (int t = 0; t < MTT; ++t) {
+    P[t] = zero4;
+    X[t] = zero4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
+  }
+
+  for (int w = 0; w < W; ++w) {
+    // next window's operands (the last window loads itself again)
+    const int wn = min(w + 1, W - 1);
+    CodeWords<BITS> cw_n;
+    i32x4_t a_n[MTT];
+    T sb_n[2], zb_n[2];
+    {
+      const uint32_t kk = lane_k(wn);
+      load_code_words<BITS>(wrow, kk, cw_n);
+#pragma unroll
+      for (int t = 0; t < MTT; ++t) a_n[t] = *reinterpret_cast<const i32x4_t*>(arow[t] + kk);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        sb_n[h] = srow[sz_index(wn, h)];
+        zb_n[h] = zrow[sz_index(wn, h)];
+      }
+    }
+
+    const i32x4_t b = expand_codes<BITS>(cw);
+    if constexpr (G32) {
+      const int passes = 64u * static_cast<uint32_t>(w) + 64u <= K ? 2 : 1;
+      for (int h = 0; h < passes; ++h) {
+        const bool mine = (j >> 1) == static_cast<uint32_t>(h);
+        const i32x4_t bh = mine ? b : zero4;
+        const i32x4_t oh = mine ? ones : zero4;
+#pragma unroll
+        for (int t = 0; t < MTT; ++t) {
+          P[t] = mfma_i8(a[t], bh, zero4);
+          X[t] = mfma_i8(a[t], oh, zero4);
+        }
+        rescale<MTT, SZ>(acc, P, X, sb[h], zb[h]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < MTT; ++t) {
+        P[t] = mfma_i8(a[t], b, P[t]);
+        X[t] = mfma_i8(a[t], ones, X[t]);
+      }
+      if (((w + 1) & ((1 << wg_shift) - 1)) == 0) {   // last window of its group
+        rescale<MTT, SZ>(acc, P, X, sb[0], zb[0]);
+#pragma unroll
+        for (int t = 0; t < MTT; ++t) {
+          P[t] = zero4;
+          X[t] = zero4;
+        }
+      }
+    }
+
+    cw = cw_n;
+#pragma unroll
+    for (int t = 0; t < MTT; ++t) a[t] = a_n[t];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sb[h] = sb_n[h];
+      zb[h] = zb_n[h];
+    }
+  }
+
+  // D layout of a 16x16 MFMA tile: lane l holds rows 4 (l / 16) + i of column l % 16
+  if (n0 + c >= p.N) return;
+  const float bias = p.bias ? act_bits_to_float<SZ>(static_cast<const T*>(p.bias)[n0 + c]) : 0.0f;
+#pragma unroll
+  for (int t = 0; t < MTT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 16 * t + 4 * static_cast<int>(j) + i;
+      if (m < p.M)
+        store_act<SZ>(p.y, static_cast<size_t>(m) * p.N + n0 + c, fmaf(p.ascale[m], acc[t][i], bias));
+    }
+  }
+}
+
+// (The launch helpers carry BITS: every width is compiled into its own
+// object, and helpers without it would be one symbol with seven bodies.)
+template <int BITS, int MTT, bool G32, int SZ>
+hipError_t launch_a8(const A8Params& p, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p.N + 63) / 64),
+                  static_cast<unsigned>((p.M + 16 * MTT - 1) / (16 * MTT)));
+  qmm_a8_kernel<BITS, MTT, G32, SZ><<<grid, dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int BITS, int MTT, bool G32>
+hipError_t launch_a8_sz(const A8Params& p, int sz, hipStream_t s) {
+  switch (sz) {
+    case ACT_F32: return launch_a8<BITS, MTT, G32, ACT_F32>(p, s);
+    case ACT_F16: return launch_a8<BITS, MTT, G32, ACT_F16>(p, s);
+    default: return launch_a8<BITS, MTT, G32, ACT_BF16>(p, s);
+  }
+}
+
+template <int BITS, int MTT>
+hipError_t launch_a8_g(const A8Params& p, int sz, hipStream_t s) {
+  return p.group == 32 ? launch_a8_sz<BITS, MTT, true>(p, sz, s)
+                       : launch_a8_sz<BITS, MTT, false>(p, sz, s);
+}
+
+#define LOWBIT_CAT2(a, b) a##b
+#define LOWBIT_CAT(a, b) LOWBIT_CAT2(a, b)
+hipError_t LOWBIT_CAT(launch_qmm_a8_b, LOWBIT_BITS)(const A8Params& p, int mtt, int sz,
+                                                   hipStream_t s) {
+  switch (mtt) {
+    case 1: return launch_a8_g<LOWBIT_BITS, 1>(p, sz, s);
+    case 2: return launch_a8_g<LOWBIT_BITS, 2>(p, sz, s);
+    default: return launch_a8_g<LOWBIT_BITS, 4>(p, sz, s);
+  }
+}
+
+}  // namespace lowbit

@@ -32,11 +32,13 @@ EXPORTED_SYMBOLS = (
     "lowbit_abi_version", "lowbit_packed_bytes", "lowbit_num_groups", "lowbit_quantize_pack",
     "lowbit_linear_workspace_bytes", "lowbit_linear", "lowbit_linear_path", "lowbit_linear_multi",
     "lowbit_status_string", "lowbit_last_error", "lowbit_linear_noalloc", "lowbit_set_tuning",
+    "lowbit_quantize_act_i8", "lowbit_linear_a8",
 )
-ABI_VERSION = 2
+ABI_VERSION = 3
 # schedule overrides (include/lowbit_tuning.h)
 TUNE_KEYS = {"qmv_block": 0, "qmv_variant": 1, "qmm_blocks": 2, "qmm_mtt": 3, "qmm_kgroups": 4,
-             "qmm_nt": 5, "qmm_waves": 6, "qmm_rgroups": 7, "qmm_small_m": 8}
+             "qmm_nt": 5, "qmm_waves": 6, "qmm_rgroups": 7, "qmm_small_m": 8,
+             "a8_mtt": 9}
 MAX_MULTI = 8   # LOWBIT_MAX_MULTI
 
 
@@ -101,6 +103,11 @@ def load() -> ctypes.CDLL:
     lib.lowbit_last_error.argtypes = []
     lib.lowbit_set_tuning.restype = ctypes.c_int
     lib.lowbit_set_tuning.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.lowbit_quantize_act_i8.restype = ctypes.c_int
+    lib.lowbit_quantize_act_i8.argtypes = [vp, ctypes.c_int, c_i64, c_i64, vp, vp, vp]
+    lib.lowbit_linear_a8.restype = ctypes.c_int
+    lib.lowbit_linear_a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, c_i64, c_i64, c_i64, vp]
     if lib.lowbit_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI version {lib.lowbit_abi_version()}, this binding "
                            f"expects {ABI_VERSION}: rebuild it with __graft_entry__.build()")
@@ -437,6 +444,61 @@ def lowbit_linear_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: torch.T
                                        _ptr(zeros), _ptr(bias), _ptr(y), bits, group, M, N, K,
                                        _stream_handle(x.device, stream))
     _check(st, "lowbit_linear_noalloc")
+    return y
+
+
+def lowbit_quantize_act_i8(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
+                           ascale: Optional[torch.Tensor] = None, stream=None):
+    """Per-row symmetric int8 codes of x[M, K] and their fp32 scales (on the GPU).
+
+    Returns (xq int8 [M, K], ascale float32 [M]); a row holding a NaN or an
+    infinity gets a NaN scale and codes 0."""
+    lib = load()
+    _expect(x.dim() == 2, "x must be 2-D [M, K]")
+    _expect(x.dtype in _DTYPE_ENUM, f"x dtype {x.dtype} is not float32, float16 or bfloat16")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if ascale is None:
+        ascale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _expect(xq.dtype == torch.int8 and tuple(xq.shape) == (M, K), f"xq must be int8 [{M}, {K}]")
+    _expect(ascale.dtype == torch.float32 and tuple(ascale.shape) == (M,),
+            f"ascale must be float32 [{M}]")
+    _require_cuda(x, xq, ascale)
+    with torch.cuda.device(x.device):
+        st = lib.lowbit_quantize_act_i8(_ptr(x), _DTYPE_ENUM[x.dtype], M, K, _ptr(xq), _ptr(ascale),
+                                        _stream_handle(x.device, stream))
+    _check(st, "lowbit_quantize_act_i8")
+    return xq, ascale
+
+
+def lowbit_linear_a8(xq: torch.Tensor, ascale: torch.Tensor, packed: torch.Tensor,
+                     scales: torch.Tensor, zeros: torch.Tensor, bias: Optional[torch.Tensor],
+                     bits: int, group: int, y: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """y = diag(ascale) . xq . dequant(packed, scales, zeros)^T (+ bias) on the
+    int8 matrix cores; y, bias, scales and zeros share one dtype."""
+    lib = load()
+    _expect(xq.dim() == 2 and xq.dtype == torch.int8, "xq must be int8 [M, K]")
+    _expect(scales.dim() == 2, "scales must be 2-D [N, K/group]")
+    M, K = xq.shape
+    N = scales.shape[0]
+    dt = scales.dtype
+    _expect(dt in _DTYPE_ENUM, f"scales dtype {dt} is not float32, float16 or bfloat16")
+    _check_weight_tensors(packed, scales, zeros, N, K, bits, group, dt)
+    _expect(ascale.dtype == torch.float32 and tuple(ascale.shape) == (M,),
+            f"ascale must be float32 [{M}]")
+    if bias is not None:
+        _expect(bias.dim() == 1 and bias.shape[0] == N and bias.dtype == dt, f"bias must be [{N}] of {dt}")
+    if y is None:
+        y = torch.empty((M, N), dtype=dt, device=xq.device)
+    _expect(y.dim() == 2 and tuple(y.shape) == (M, N) and y.dtype == dt, f"y must be [{M}, {N}] of {dt}")
+    _require_cuda(xq, ascale, packed, scales, zeros, bias, y)
+    with torch.cuda.device(xq.device):
+        st = lib.lowbit_linear_a8(_ptr(xq), _ptr(ascale), _ptr(packed), _ptr(scales), _ptr(zeros),
+                                  _ptr(bias), _ptr(y), _DTYPE_ENUM[dt], bits, group, M, N, K,
+                                  _stream_handle(xq.device, stream))
+    _check(st, "lowbit_linear_a8")
     return y
 
 

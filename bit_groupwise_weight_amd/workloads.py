@@ -166,6 +166,16 @@ def mixed_sweep() -> List[Case]:
     return out
 
 
+def activation_quantized() -> List[Case]:
+    """The activation-quantized variant (8-bit dynamic activations with 4-bit
+    weights in groups of 32, the export mode of "[MPS] Add support for Int4
+    groupwise quantization") at the batched Llama-3.1-8B MLP shapes: M=128,
+    bf16 activations x ~ N(0,1), W ~ N(0,0.02).  Not part of WORKLOADS: these
+    cases run through the int8-activation entry points, not lowbit_linear."""
+    return [Case(f"a8_m128_k{K}_n{N}_b4_g32", 128, K, N, 4, 32, "bf16")
+            for (K, N) in [(4096, 14336), (14336, 4096)]]
+
+
 WORKLOADS = {
     "single_qmv": single_qmv,
     "llama8b_decode": llama8b_decode,

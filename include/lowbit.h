@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 2
+#define LOWBIT_ABI_VERSION 3
 
 typedef enum lowbit_status {
   LOWBIT_OK = 0,
@@ -226,6 +226,55 @@ typedef struct lowbit_linear_desc {
  * on each desc.  Enqueued on `stream`; asynchronous. */
 lowbit_status lowbit_linear_multi(const lowbit_linear_desc* descs, int count, lowbit_dtype act_dtype,
                                   int bits, int group, int64_t M, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Activation-quantized variant: 8-bit dynamic activations with the groupwise
+ * low-bit weights above ("[MPS] Add support for Int4 groupwise quantization":
+ * the export mode with 8-bit dynamic activations and 4-bit weights in groups
+ * of 32; the page names the mode only, and these conventions fix it):
+ *   - each activation row m is quantized at run time, symmetric, with one
+ *     fp32 scale: a_m = max_k |x[m, k]| / 127 (correctly rounded fp32
+ *     divide), xq[m, k] = clamp(rint_half_even(x[m, k] / a_m), -127, 127)
+ *     (fp32 divide); a row whose a_m is 0 gets codes 0; a row holding a NaN
+ *     or an infinity gets a_m = NaN and codes 0;
+ *   - y[m, n] = a_m * sum_k xq[m, k] * w[n, k] (+ bias[n]), w = s*q + z as
+ *     above (any bit width and group size).
+ * ---------------------------------------------------------------------- */
+
+/* Quantize activation rows to int8 (the first step of the variant).
+ *
+ *   x        device, M x K row-major, act_dtype, 16-byte aligned; values are
+ *            taken exactly as fp32.
+ *   M >= 0 (0 is a no-op), K > 0 and a multiple of 32 (at most 2^30).
+ *   xq       device, M x K int8 row-major, 16-byte aligned.  Written.
+ *   ascale   device, M fp32, 4-byte aligned.  Written.
+ *
+ * Asynchronous (enqueued on `stream`); codes and scales are bitwise
+ * determined by x.  Non-finite values are not an error: their row is marked
+ * by a NaN scale. */
+lowbit_status lowbit_quantize_act_i8(const void* x, lowbit_dtype act_dtype, int64_t M, int64_t K,
+                                     int8_t* xq, float* ascale, void* stream);
+
+/* y = diag(ascale) . xq . dequant(packed, scales, zeros)^T (+ bias) on the
+ * int8 matrix cores: per group the exact int32 sums of xq * q and of xq, each
+ * turned into fp32 and scaled by the group's scale and zero; ascale and the
+ * bias enter once in fp32 and the result is rounded to dtype to nearest even.
+ *
+ *   xq, ascale   as written by lowbit_quantize_act_i8 (xq 16-byte aligned).
+ *   packed, scales, zeros   as for lowbit_linear, scales and zeros in dtype;
+ *            packed 16-byte aligned.
+ *   bias     device, N elements of dtype, or NULL.
+ *   y        device, M x N row-major, dtype.  Overwritten; must not alias an
+ *            input.
+ *   dtype    storage type of scales, zeros, bias and y (fp32, fp16, bf16).
+ *   M >= 0 (0 is a no-op), N > 0, K % group == 0, M <= 2^20.
+ *
+ * No workspace, one launch, asynchronous.  Deterministic: no atomics, and
+ * every output is summed in one fixed order. */
+lowbit_status lowbit_linear_a8(const int8_t* xq, const float* ascale, const uint8_t* packed,
+                               const void* scales, const void* zeros, const void* bias, void* y,
+                               lowbit_dtype dtype, int bits, int group, int64_t M, int64_t N,
+                               int64_t K, void* stream);
 
 /* Static text for a status code. */
 const char* lowbit_status_string(lowbit_status status);

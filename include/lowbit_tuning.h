@@ -33,7 +33,9 @@ typedef enum lowbit_tuning_key {
   LOWBIT_TUNE_QMM_RGROUPS = 7,  /* bf16 MFMA kernel: 1 or 2 row groups of 4 waves   */
   LOWBIT_TUNE_QMM_SMALL_M = 8,  /* fp16: largest M of the small-M MFMA kernel (1-16;
                                    1 = not used)                                    */
-  LOWBIT_TUNE_COUNT = 9
+  LOWBIT_TUNE_A8_MTT = 9,       /* int8-activation linear: 16-row tiles per block
+                                   (1, 2 or 4)                                      */
+  LOWBIT_TUNE_COUNT = 10
 } lowbit_tuning_key;
 
 /* Set (value > 0) or clear (value == 0) one override.  LOWBIT_ERR_INVALID_ARG

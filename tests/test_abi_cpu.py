@@ -34,7 +34,7 @@ def test_header_and_binding_agree():
 def test_library_exports_every_declared_symbol(lowbit_lib):
     for name in declared_functions():
         assert hasattr(lowbit_lib, name), name
-    assert lowbit_lib.lowbit_abi_version() == 2
+    assert lowbit_lib.lowbit_abi_version() == 3
     plib = probe.load()
     for name in declared_functions("probe"):
         assert hasattr(plib, name), name
@@ -78,6 +78,44 @@ def lin(lib, **kw):
 ])
 def test_linear_validation(lowbit_lib, kw, status):
     assert lin(lowbit_lib, **kw) == status
+
+
+def actq(lib, **kw):
+    a = dict(x=A, act=BF16, M=4, K=256, xq=A, ascale=A)
+    a.update(kw)
+    return lib.lowbit_quantize_act_i8(a["x"], a["act"], a["M"], a["K"], a["xq"], a["ascale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act=3), UNSUPPORTED), (dict(M=-1), INVALID), (dict(K=0), INVALID), (dict(K=48), INVALID),
+    (dict(K=(1 << 30) + 32), INVALID), (dict(x=None), INVALID), (dict(xq=None), INVALID),
+    (dict(ascale=None), INVALID), (dict(x=A + 8), MISALIGNED), (dict(xq=A + 4), MISALIGNED),
+    (dict(ascale=A + 2), MISALIGNED), (dict(M=0), OK), (dict(M=0, x=None, xq=None), OK),
+])
+def test_quantize_act_validation(lowbit_lib, kw, status):
+    assert actq(lowbit_lib, **kw) == status
+
+
+def lin_a8(lib, **kw):
+    a = dict(xq=A, ascale=A, packed=A, scales=A, zeros=A, bias=None, y=A, dt=BF16, bits=4,
+             group=32, M=4, N=64, K=256)
+    a.update(kw)
+    return lib.lowbit_linear_a8(a["xq"], a["ascale"], a["packed"], a["scales"], a["zeros"],
+                                a["bias"], a["y"], a["dt"], a["bits"], a["group"], a["M"], a["N"],
+                                a["K"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=0), INVALID), (dict(bits=8), INVALID), (dict(group=16), INVALID),
+    (dict(K=96, group=64), INVALID), (dict(N=0), INVALID), (dict(M=-1), INVALID),
+    (dict(M=(1 << 20) + 1), INVALID), (dict(xq=None), INVALID), (dict(ascale=None), INVALID),
+    (dict(y=None), INVALID), (dict(packed=None), INVALID), (dict(zeros=None), INVALID),
+    (dict(dt=5), UNSUPPORTED), (dict(xq=A + 4), MISALIGNED), (dict(packed=A + 4), MISALIGNED),
+    (dict(ascale=A + 2), MISALIGNED), (dict(y=A + 1), MISALIGNED), (dict(bias=A + 1), MISALIGNED),
+    (dict(M=0), OK), (dict(M=0, xq=None, ascale=None, y=None), OK), (dict(M=0, packed=None), INVALID),
+])
+def test_linear_a8_validation(lowbit_lib, kw, status):
+    assert lin_a8(lowbit_lib, **kw) == status
     if status != OK:
         assert lb.lowbit_last_error() != ""
 
@@ -140,7 +178,8 @@ def test_quantize_validation(lowbit_lib, args, status):
 
 
 def test_tuning_validation(lowbit_lib):
-    assert lowbit_lib.lowbit_set_tuning(9, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(10, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(9, 2) == OK and lowbit_lib.lowbit_set_tuning(9, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(7, 2) == OK and lowbit_lib.lowbit_set_tuning(7, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(-1, 1) == INVALID
     assert lowbit_lib.lowbit_set_tuning(0, -2) == INVALID
