@@ -41,6 +41,7 @@ from bit_groupwise_weight_amd import probe  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+MFMA_I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 ROTATE_BYTES = 1 << 30
 
 # HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes (and
@@ -86,6 +87,8 @@ def parse():
                          "and grid of the b=4 decode case, which a kernel trace would mix up)")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the one-call-per-launch timing (profiling runs: only graph launches)")
+    ap.add_argument("--no-a8", action="store_true",
+                    help="skip the activation-quantized variant (int8 dynamic activations)")
     ap.add_argument("--no-floor", action="store_true",
                     help="skip the streaming-read and load-latency measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -204,6 +207,56 @@ def time_eager(p, reps, stream, prepared=True):
 LAYER_SHAPES = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
                 ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
 LAYER_BITS, LAYER_GROUP = 4, 64
+
+
+def prepare_a8(case, copies, dev):
+    """Weights as prepare(); int8 activation buffers for the quantizer's output."""
+    p = prepare(case, copies, dev)
+    p["xq"] = torch.empty((case.M, case.K), dtype=torch.int8, device=dev)
+    p["ascale"] = torch.empty((case.M,), dtype=torch.float32, device=dev)
+    return p
+
+
+def launch_a8(p, i, stream, quant=True, linear=True):
+    """The activation-quantized variant on weight copy i: the per-row int8
+    quantizer, then the int8 linear."""
+    from bit_groupwise_weight_amd import lowbit as lb
+    c = p["case"]
+    if quant:
+        lb.lowbit_quantize_act_i8(p["x"], p["xq"], p["ascale"], stream=stream)
+    if linear:
+        packed, s, z = p["sets"][i % len(p["sets"])]
+        lb.lowbit_linear_a8(p["xq"], p["ascale"], packed, s, z, p["bias"], c.bits, c.group,
+                            y=p["ys"][i % 2], stream=stream)
+
+
+def activation_quantized(dev, stream, reps):
+    """Graph-timed quantizer, linear and whole call at the batched Llama-3.1-8B
+    MLP shapes (M=128, bits 4, group 32, bf16)."""
+    from bit_groupwise_weight_amd.workloads import activation_quantized as a8_cases
+    rows = []
+    for c in a8_cases():
+        p = prepare_a8(c, copies_for(c), dev)
+        torch.cuda.synchronize()
+        n = len(p["sets"])
+        reps_n = max(2, reps // n + 1)
+        t = {}
+        for key, kw in (("quant_us", dict(linear=False)), ("linear_us", dict(quant=False)),
+                        ("call_us", {})):
+            g = capture(lambda i, s, kw=kw: launch_a8(p, i, s, **kw), n, stream)
+            t[key] = time_graph(g, reps_n, n, stream)
+            del g
+        del p
+        torch.cuda.empty_cache()
+        ops = 2.0 * c.M * c.N * c.K
+        tops = ops / (t["linear_us"] * 1e-6) / 1e12
+        rows.append({"K": c.K, "N": c.N, "M": c.M, "bits": c.bits, "group": c.group,
+                     **{k: round(v, 3) for k, v in t.items()},
+                     "TOP_s": round(tops, 2), "frac_i8_peak": round(tops / MFMA_I8_PEAK_TOPS, 4),
+                     "TOP_s_call": round(ops / (t["call_us"] * 1e-6) / 1e12, 2)})
+        log(f"a8 K={c.K} N={c.N}: quant {t['quant_us']:.2f} us, linear {t['linear_us']:.2f} us "
+            f"({tops:.1f} TOP/s), call {t['call_us']:.2f} us")
+    return rows
 
 
 def prepare_layer(copies, dev):
@@ -616,6 +669,8 @@ def main():
             "linear_only_us_per_token_32_layers": round(32 * fus_us, 2),
         }
 
+    a8 = None if args.no_a8 else activation_quantized(dev, stream, args.reps)
+
     floor = None
     if not args.no_floor:
         floor = single_launch_floor([algo_bytes(c) for c in qcases], qmv_us, dev, stream, args.reps)
@@ -675,6 +730,23 @@ def main():
                               "profile of the same kernel sources; null for other sources",
         },
         "qmm": qmm,
+        "activation_quantized": None if a8 is None else {
+            "method": "8-bit dynamic activations (per-row symmetric int8, fp32 scale) x "
+                      "groupwise low-bit weights on the int8 MFMA; M=128 bf16 x ~ N(0,1), "
+                      "bits 4, group 32 (the -qmode 8da4w -G 32 export mode)",
+            "cases": a8,
+        },
+        "roofline_a8": None if a8 is None else {
+            "kernel": "qmm_a8 (int8 activations x 4-bit codes, group 32, M=128)",
+            "bound": "mfma",
+            "achieved": round(sum(2.0 * r["M"] * r["N"] * r["K"] for r in a8)
+                              / (sum(r["linear_us"] for r in a8) * 1e-6) / 1e12, 2),
+            "peak": MFMA_I8_PEAK_TOPS,
+            "unit": "TOP/s",
+            "frac": round(sum(2.0 * r["M"] * r["N"] * r["K"] for r in a8)
+                          / (sum(r["linear_us"] for r in a8) * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS, 4),
+            "traffic": None,
+        },
         "qmv_eager_us_per_call": None if eager_us is None else [round(u, 3) for u in eager_us],
         "qmv_eager_us_per_call_generic": None if eager_generic_us is None
         else [round(u, 3) for u in eager_generic_us],

@@ -45,7 +45,8 @@ def _units():
              ("device_scratch.hip", "device_scratch.o", []),
              ("act_quant.hip", "act_quant.o", ["-ffp-contract=off"])]
     for b in range(1, 8):
-        units.append(("qmm_a8.hip", f"qmm_a8_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
+        units.append(("qmm_a8.hip", f"qmm_a8_b{b}.o",
+                      [f"-DLOWBIT_BITS={b}", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]))
         units.append(("qmv.hip", f"qmv_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
         units.append(("qmm.hip", f"qmm_b{b}.o", [f"-DLOWBIT_BITS={b}"]))
         units.append(("qmm_bf16.hip", f"qmm_bf16_b{b}.o",

@@ -176,15 +176,15 @@ struct A8Params {
   int group;
   int64_t row_bytes;      // K * bits / 8
 };
-// Blocks of 4 waves, one 16-column MFMA tile per wave, `mtt` (1, 2 or 4)
-// 16-row tiles per block: grid (ceil(N / 64), ceil(M / (16 * mtt))).
-hipError_t launch_qmm_a8_b1(const A8Params&, int mtt, int sz, hipStream_t);
-hipError_t launch_qmm_a8_b2(const A8Params&, int mtt, int sz, hipStream_t);
-hipError_t launch_qmm_a8_b3(const A8Params&, int mtt, int sz, hipStream_t);
-hipError_t launch_qmm_a8_b4(const A8Params&, int mtt, int sz, hipStream_t);
-hipError_t launch_qmm_a8_b5(const A8Params&, int mtt, int sz, hipStream_t);
-hipError_t launch_qmm_a8_b6(const A8Params&, int mtt, int sz, hipStream_t);
-hipError_t launch_qmm_a8_b7(const A8Params&, int mtt, int sz, hipStream_t);
+// Blocks of 4 waves, `nt` (1 or 2) 16-column MFMA tiles per wave, `mtt`
+// (1, 2 or 4) 16-row tiles per block: grid (ceil(N / (64 nt)), ceil(M / (16 mtt))).
+hipError_t launch_qmm_a8_b1(const A8Params&, int mtt, int nt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b2(const A8Params&, int mtt, int nt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b3(const A8Params&, int mtt, int nt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b4(const A8Params&, int mtt, int nt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b5(const A8Params&, int mtt, int nt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b6(const A8Params&, int mtt, int nt, int sz, hipStream_t);
+hipError_t launch_qmm_a8_b7(const A8Params&, int mtt, int nt, int sz, hipStream_t);
 
 // ------------------------------------------------- library-owned scratch --
 // Size of the device array behind lowbit_linear_noalloc (per device).  The

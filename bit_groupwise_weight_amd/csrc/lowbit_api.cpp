@@ -500,7 +500,7 @@ lowbit_status run_qmm(const void* x, lowbit_dtype act, const uint8_t* packed, co
   return LOWBIT_OK;
 }
 
-typedef hipError_t (*A8Launcher)(const lowbit::A8Params&, int, int, hipStream_t);
+typedef hipError_t (*A8Launcher)(const lowbit::A8Params&, int, int, int, hipStream_t);
 const A8Launcher kA8[8] = {nullptr,
                            lowbit::launch_qmm_a8_b1,
                            lowbit::launch_qmm_a8_b2,
@@ -513,18 +513,34 @@ const A8Launcher kA8[8] = {nullptr,
 // Largest M of the int8-activation linear: 65535 blocks of 16 rows.
 constexpr int64_t kA8MaxM = int64_t(1) << 20;
 
-// 16-row tiles per block of the int8-activation linear: the most (4, 2, 1)
-// that still leaves two waves per SIMD (each wave is one 16-column tile),
-// and no more than the rows need.
-int a8_row_tiles(int64_t M, int64_t N) {
-  const int forced = tuning(LOWBIT_TUNE_A8_MTT, 0);
-  if (forced == 1 || forced == 2 || forced == 4) return forced;
-  const int64_t col_waves = (N + 15) / 16;
-  const int64_t target = int64_t(8) * device_cus();
-  int mtt = 4;
-  while (mtt > 1 && (16 * (mtt / 2) >= M || col_waves * ((M + 16 * mtt - 1) / (16 * mtt)) < target))
-    mtt /= 2;
-  return mtt;
+// Tiles of the int8-activation linear: 16-row tiles per block (mtt) and
+// 16-column tiles per wave (nt).  The kernel is bound by its vector-memory
+// instructions; per 16 x 16 output tile and 64-wide K window it issues about
+// 1/nt activation loads, 1/mtt code loads and 1/4 scale/zero loads, so the
+// largest tiles win as long as the launch keeps at least 3.5 waves per CU
+// (measured at M = 128, bits 4, group 32: K = 4096, N = 14336 runs fastest
+// with mtt 4, nt 2 at 3.5 waves per CU, 67 us against 84 us with mtt 2, nt 2
+// at 7; K = 14336, N = 4096 with mtt 2, nt 1 at 4 waves per CU, 92 us,
+// against 132-210 us for larger tiles at 2 waves per CU).
+constexpr int kA8HalfWavesPerCu = 7;
+void a8_tiles(int64_t M, int64_t N, int* mtt_out, int* nt_out) {
+  static const int kOrder[][2] = {{4, 2}, {2, 2}, {4, 1}, {2, 1}, {1, 2}, {1, 1}};
+  const int64_t target = (int64_t(kA8HalfWavesPerCu) * device_cus() + 1) / 2;
+  int mtt = 1, nt = 1;
+  for (const auto& c : kOrder) {
+    if (c[0] > 1 && 16 * (c[0] / 2) >= M) continue;   // the rows fit in half the tiles
+    const int64_t waves = ((N + 16 * c[1] - 1) / (16 * c[1])) * ((M + 16 * c[0] - 1) / (16 * c[0]));
+    if (waves >= target) {
+      mtt = c[0];
+      nt = c[1];
+      break;
+    }
+  }
+  const int fm = tuning(LOWBIT_TUNE_A8_MTT, 0), fn = tuning(LOWBIT_TUNE_A8_NT, 0);
+  if (fm == 1 || fm == 2 || fm == 4) mtt = fm;
+  if (fn == 1 || fn == 2) nt = fn;
+  *mtt_out = mtt;
+  *nt_out = nt;
 }
 
 }  // namespace
@@ -756,7 +772,9 @@ lowbit_status lowbit_linear_a8(const int8_t* xq, const float* ascale, const uint
   p.groups = static_cast<int>(K / group);
   p.group = group;
   p.row_bytes = K * bits / 8;
-  const hipError_t he = kA8[bits](p, a8_row_tiles(M, N), act_kind(dtype), static_cast<hipStream_t>(stream));
+  int mtt = 1, nt = 1;
+  a8_tiles(M, N, &mtt, &nt);
+  const hipError_t he = kA8[bits](p, mtt, nt, act_kind(dtype), static_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "qmm_a8 launch");
   return LOWBIT_OK;
 }

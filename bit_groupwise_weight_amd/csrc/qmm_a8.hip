@@ -24,10 +24,19 @@
 // lane groups; a row of K = 64 w + 32 ends with a half window, whose missing
 // half the lanes read from the window's first half and mask out.
 //
-// Block: 4 waves, each one 16-column tile over MTT 16-row tiles and all of
-// K; the next window's codes, activations and scales are loaded before the
-// current window is multiplied.  No LDS and no barriers: a wave past N
-// returns at once.
+// Block: 4 waves, each NT 16-column tiles over MTT 16-row tiles and all of
+// K (the activation operand and its row sums X serve the NT column tiles).
+// The operands of 8 / MTT windows are loaded one such batch ahead.  No LDS
+// and no barriers: a wave past N returns at once.
+//
+// What bounds it: the vector-memory address unit, not the MFMAs (counters at
+// M = 128, K = 4096, N = 14336 with one column tile and one load per scale:
+// the address unit busy 82 % of the kernel and stalled on the cache 55 %,
+// VALU and MFMA mostly idle).  Every load instruction occupies it about the
+// same whatever its width, so the kernel issues few, wide ones: per 16 x 16
+// output tile and window about 1/NT activation loads, 1/MTT code loads and
+// (groups of 32) 1/4 scale/zero loads, the scales and zeros of a batch
+// coming as one vector per column tile.
 #include "qmm_common.h"
 
 #ifndef LOWBIT_BITS
@@ -115,34 +124,26 @@ __device__ __forceinline__ i32x4_t expand_codes(const CodeWords<BITS>& cw) {
   }
 }
 
-template <int MTT, int SZ, typename T>
-__device__ __forceinline__ void rescale(float (&acc)[MTT][4], const i32x4_t (&P)[MTT],
-                                        const i32x4_t (&X)[MTT], T sb, T zb) {
-  const float s = act_bits_to_float<SZ>(sb);
-  const float z = act_bits_to_float<SZ>(zb);
-#pragma unroll
-  for (int t = 0; t < MTT; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[t][i] = fmaf(s, static_cast<float>(P[t][i]), acc[t][i]);
-      acc[t][i] = fmaf(z, static_cast<float>(X[t][i]), acc[t][i]);
-    }
-  }
-}
-
-template <int BITS, int MTT, bool G32, int SZ>
+template <int BITS, int MTT, int NT, bool G32, int SZ>
 __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
   using T = typename Act<SZ>::bits_t;
+  constexpr int TB = static_cast<int>(sizeof(T));
   const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 * NT;
   if (n0 >= p.N) return;
   const int c = lane & 15;
   const uint32_t j = lane >> 4;
   const int m0 = blockIdx.y * 16 * MTT;
-  const int nc = min(n0 + c, p.N - 1);
-  const uint8_t* wrow = p.packed + static_cast<size_t>(nc) * p.row_bytes;
-  const T* srow = static_cast<const T*>(p.scales) + static_cast<size_t>(nc) * p.groups;
-  const T* zrow = static_cast<const T*>(p.zeros) + static_cast<size_t>(nc) * p.groups;
+  const uint8_t* wrow[NT];
+  const T* srow[NT];
+  const T* zrow[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const int nc = min(n0 + 16 * q + c, p.N - 1);
+    wrow[q] = p.packed + static_cast<size_t>(nc) * p.row_bytes;
+    srow[q] = static_cast<const T*>(p.scales) + static_cast<size_t>(nc) * p.groups;
+    zrow[q] = static_cast<const T*>(p.zeros) + static_cast<size_t>(nc) * p.groups;
+  }
   const int8_t* arow[MTT];
 #pragma unroll
   for (int t = 0; t < MTT; ++t)
@@ -166,136 +167,229 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
     return G32 ? min(2 * w + h, p.groups - 1) : (w >> wg_shift);
   };
 
-  CodeWords<BITS> cw;
-  i32x4_t a[MTT];
-  T sb[2], zb[2];
-  {
-    const uint32_t kk = lane_k(0);
-    load_code_words<BITS>(wrow, kk, cw);
+  // Operands of U consecutive windows (U = 8 / MTT: the activations of a
+  // batch take 64 registers at every MTT), loaded one batch ahead.  The
+  // scales and zeros of a batch are kept as raw words, SG values of T per
+  // column tile (two per window with groups of 32, else one).
+  constexpr int U = 8 / MTT;
+  constexpr int SG = G32 ? 2 * U : U;
+  constexpr int SZW = (SG * TB + 3) / 4;
+  struct Batch {
+    CodeWords<BITS> cw[U][NT];
+    i32x4_t a[U][MTT];
+    uint32_t sw[NT][SZW], zw[NT][SZW];
+  };
+  // Groups of 32: the 2U scales (and zeros) of a batch are contiguous in the
+  // row and come in one vector load per column tile when their start is
+  // 4-byte aligned and the batch lies inside the row (every load instruction
+  // costs the address unit about the same, whatever its width); otherwise
+  // one load per group.
+  const bool sz_wide = G32 && (TB == 4 || (p.groups % 2 == 0)) &&
+                       ((reinterpret_cast<uintptr_t>(p.scales) | reinterpret_cast<uintptr_t>(p.zeros)) & 3u) == 0;
+  auto load_words = [&](const T* src, uint32_t (&wd)[SZW]) {
+    const uint32_t* s4 = static_cast<const uint32_t*>(__builtin_assume_aligned(src, 4));
+    if constexpr (SZW % 4 == 0) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int t = 0; t < MTT; ++t) a[t] = *reinterpret_cast<const i32x4_t*>(arow[t] + kk);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sb[h] = srow[sz_index(0, h)];
-      zb[h] = zrow[sz_index(0, h)];
-    }
-  }
-
-  float acc[MTT][4];
-  i32x4_t P[MTT], X[MTT];
-#pragma unroll
-  for (int t = 0; t < MTT; ++t) {
-    P[t] = zero4;
-    X[t] = zero4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-  }
-
-  for (int w = 0; w < W; ++w) {
-    // next window's operands (the last window loads itself again)
-    const int wn = min(w + 1, W - 1);
-    CodeWords<BITS> cw_n;
-    i32x4_t a_n[MTT];
-    T sb_n[2], zb_n[2];
-    {
-      const uint32_t kk = lane_k(wn);
-      load_code_words<BITS>(wrow, kk, cw_n);
-#pragma unroll
-      for (int t = 0; t < MTT; ++t) a_n[t] = *reinterpret_cast<const i32x4_t*>(arow[t] + kk);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        sb_n[h] = srow[sz_index(wn, h)];
-        zb_n[h] = zrow[sz_index(wn, h)];
-      }
-    }
-
-    const i32x4_t b = expand_codes<BITS>(cw);
-    if constexpr (G32) {
-      const int passes = 64u * static_cast<uint32_t>(w) + 64u <= K ? 2 : 1;
-      for (int h = 0; h < passes; ++h) {
-        const bool mine = (j >> 1) == static_cast<uint32_t>(h);
-        const i32x4_t bh = mine ? b : zero4;
-        const i32x4_t oh = mine ? ones : zero4;
-#pragma unroll
-        for (int t = 0; t < MTT; ++t) {
-          P[t] = mfma_i8(a[t], bh, zero4);
-          X[t] = mfma_i8(a[t], oh, zero4);
-        }
-        rescale<MTT, SZ>(acc, P, X, sb[h], zb[h]);
+      for (int q = 0; q < SZW / 4; ++q) {
+        u32x4 v;
+        __builtin_memcpy(&v, s4 + 4 * q, 16);
+        wd[4 * q] = v.x; wd[4 * q + 1] = v.y; wd[4 * q + 2] = v.z; wd[4 * q + 3] = v.w;
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < MTT; ++t) {
-        P[t] = mfma_i8(a[t], b, P[t]);
-        X[t] = mfma_i8(a[t], ones, X[t]);
-      }
-      if (((w + 1) & ((1 << wg_shift) - 1)) == 0) {   // last window of its group
-        rescale<MTT, SZ>(acc, P, X, sb[0], zb[0]);
+      for (int q = 0; q < SZW; ++q) wd[q] = s4[q];
+    }
+  };
+  auto load_batch = [&](int bi, Batch& bt) {
+    bool wide = false;
+    if constexpr (G32) {
+      const int g0 = SG * bi;
+      if (sz_wide && g0 + SG <= p.groups) {
+        wide = true;
 #pragma unroll
-        for (int t = 0; t < MTT; ++t) {
-          P[t] = zero4;
-          X[t] = zero4;
+        for (int q = 0; q < NT; ++q) {
+          load_words(srow[q] + g0, bt.sw[q]);
+          load_words(zrow[q] + g0, bt.zw[q]);
         }
       }
     }
-
-    cw = cw_n;
+    if (!wide) {
 #pragma unroll
-    for (int t = 0; t < MTT; ++t) a[t] = a_n[t];
+      for (int q = 0; q < NT; ++q) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sb[h] = sb_n[h];
-      zb[h] = zb_n[h];
+        for (int i = 0; i < SZW; ++i) {
+          bt.sw[q][i] = 0u;
+          bt.zw[q][i] = 0u;
+        }
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+          const int w = min(bi * U + (G32 ? g / 2 : g), W - 1);
+          const int idx = sz_index(w, G32 ? g % 2 : 0);
+          const uint32_t sh = 8u * static_cast<uint32_t>((g * TB) % 4);
+          bt.sw[q][(g * TB) / 4] |= static_cast<uint32_t>(srow[q][idx]) << sh;
+          bt.zw[q][(g * TB) / 4] |= static_cast<uint32_t>(zrow[q][idx]) << sh;
+        }
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = min(bi * U + u, W - 1);
+      const uint32_t kk = lane_k(w);
+#pragma unroll
+      for (int q = 0; q < NT; ++q) load_code_words<BITS>(wrow[q], kk, bt.cw[u][q]);
+#pragma unroll
+      for (int t = 0; t < MTT; ++t) bt.a[u][t] = *reinterpret_cast<const i32x4_t*>(arow[t] + kk);
+    }
+  };
+  // value g (0 .. SG-1) of a batch's raw words, as fp32
+  auto sz_value = [&](const uint32_t (&wd)[SZW], int g) -> float {
+    if constexpr (TB == 4) return __uint_as_float(wd[g]);
+    else return act_bits_to_float<SZ>((wd[g >> 1] >> (16 * (g & 1))) & 0xffffu);
+  };
+
+  // group-32 passes: the lane groups of pass h are 2h and 2h + 1
+  const i32x4_t keep0 = (j >> 1) == 0 ? i32x4_t{-1, -1, -1, -1} : zero4;
+  const i32x4_t keep1 = (j >> 1) == 1 ? i32x4_t{-1, -1, -1, -1} : zero4;
+  const i32x4_t ones0 = ones & keep0, ones1 = ones & keep1;
+
+  float acc[MTT][NT][4];
+  i32x4_t P[MTT][NT], X[MTT];
+#pragma unroll
+  for (int t = 0; t < MTT; ++t) {
+    X[t] = zero4;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      P[t][q] = zero4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][q][i] = 0.0f;
+    }
+  }
+  // acc += s * P + z * X for every tile (X converted once per row tile)
+  auto rescale = [&](const Batch& bt, int g) {
+#pragma unroll
+    for (int t = 0; t < MTT; ++t) {
+      float xf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[i] = static_cast<float>(X[t][i]);
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        const float sv = sz_value(bt.sw[q], g), zv = sz_value(bt.zw[q], g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[t][q][i] = fmaf(sv, static_cast<float>(P[t][q][i]), acc[t][q][i]);
+          acc[t][q][i] = fmaf(zv, xf[i], acc[t][q][i]);
+        }
+      }
+    }
+  };
+
+  const int NB = (W + U - 1) / U;
+  Batch cur;
+  load_batch(0, cur);
+  for (int bi = 0; bi < NB; ++bi) {
+    Batch nxt;
+    load_batch(min(bi + 1, NB - 1), nxt);   // the last batch loads itself again
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = bi * U + u;
+      if (w >= W) break;
+      i32x4_t b[NT];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) b[q] = expand_codes<BITS>(cur.cw[u][q]);
+      if constexpr (G32) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && 64u * static_cast<uint32_t>(w) + 64u > K) break;   // a half window
+          const i32x4_t keep = h == 0 ? keep0 : keep1;
+          const i32x4_t oh = h == 0 ? ones0 : ones1;
+#pragma unroll
+          for (int t = 0; t < MTT; ++t) {
+            X[t] = mfma_i8(cur.a[u][t], oh, zero4);
+#pragma unroll
+            for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(cur.a[u][t], b[q] & keep, zero4);
+          }
+          rescale(cur, 2 * u + h);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < MTT; ++t) {
+          X[t] = mfma_i8(cur.a[u][t], ones, X[t]);
+#pragma unroll
+          for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(cur.a[u][t], b[q], P[t][q]);
+        }
+        if (((w + 1) & ((1 << wg_shift) - 1)) == 0) {   // last window of its group
+          rescale(cur, u);
+#pragma unroll
+          for (int t = 0; t < MTT; ++t) {
+            X[t] = zero4;
+#pragma unroll
+            for (int q = 0; q < NT; ++q) P[t][q] = zero4;
+          }
+        }
+      }
+    }
+    cur = nxt;
   }
 
   // D layout of a 16x16 MFMA tile: lane l holds rows 4 (l / 16) + i of column l % 16
-  if (n0 + c >= p.N) return;
-  const float bias = p.bias ? act_bits_to_float<SZ>(static_cast<const T*>(p.bias)[n0 + c]) : 0.0f;
 #pragma unroll
-  for (int t = 0; t < MTT; ++t) {
+  for (int q = 0; q < NT; ++q) {
+    const int n = n0 + 16 * q + c;
+    if (n >= p.N) break;
+    const float bias = p.bias ? act_bits_to_float<SZ>(static_cast<const T*>(p.bias)[n]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 16 * t + 4 * static_cast<int>(j) + i;
-      if (m < p.M)
-        store_act<SZ>(p.y, static_cast<size_t>(m) * p.N + n0 + c, fmaf(p.ascale[m], acc[t][i], bias));
+    for (int t = 0; t < MTT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * t + 4 * static_cast<int>(j) + i;
+        if (m < p.M)
+          store_act<SZ>(p.y, static_cast<size_t>(m) * p.N + n, fmaf(p.ascale[m], acc[t][q][i], bias));
+      }
     }
   }
 }
 
 // (The launch helpers carry BITS: every width is compiled into its own
 // object, and helpers without it would be one symbol with seven bodies.)
-template <int BITS, int MTT, bool G32, int SZ>
+template <int BITS, int MTT, int NT, bool G32, int SZ>
 hipError_t launch_a8(const A8Params& p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((p.N + 63) / 64),
+  const dim3 grid(static_cast<unsigned>((p.N + 64 * NT - 1) / (64 * NT)),
                   static_cast<unsigned>((p.M + 16 * MTT - 1) / (16 * MTT)));
-  qmm_a8_kernel<BITS, MTT, G32, SZ><<<grid, dim3(256), 0, s>>>(p);
+  qmm_a8_kernel<BITS, MTT, NT, G32, SZ><<<grid, dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <int BITS, int MTT, bool G32>
+template <int BITS, int MTT, int NT, bool G32>
 hipError_t launch_a8_sz(const A8Params& p, int sz, hipStream_t s) {
   switch (sz) {
-    case ACT_F32: return launch_a8<BITS, MTT, G32, ACT_F32>(p, s);
-    case ACT_F16: return launch_a8<BITS, MTT, G32, ACT_F16>(p, s);
-    default: return launch_a8<BITS, MTT, G32, ACT_BF16>(p, s);
+    case ACT_F32: return launch_a8<BITS, MTT, NT, G32, ACT_F32>(p, s);
+    case ACT_F16: return launch_a8<BITS, MTT, NT, G32, ACT_F16>(p, s);
+    default: return launch_a8<BITS, MTT, NT, G32, ACT_BF16>(p, s);
   }
 }
 
-template <int BITS, int MTT>
+template <int BITS, int MTT, int NT>
 hipError_t launch_a8_g(const A8Params& p, int sz, hipStream_t s) {
-  return p.group == 32 ? launch_a8_sz<BITS, MTT, true>(p, sz, s)
-                       : launch_a8_sz<BITS, MTT, false>(p, sz, s);
+  return p.group == 32 ? launch_a8_sz<BITS, MTT, NT, true>(p, sz, s)
+                       : launch_a8_sz<BITS, MTT, NT, false>(p, sz, s);
 }
 
 #define LOWBIT_CAT2(a, b) a##b
 #define LOWBIT_CAT(a, b) LOWBIT_CAT2(a, b)
-hipError_t LOWBIT_CAT(launch_qmm_a8_b, LOWBIT_BITS)(const A8Params& p, int mtt, int sz,
+hipError_t LOWBIT_CAT(launch_qmm_a8_b, LOWBIT_BITS)(const A8Params& p, int mtt, int nt, int sz,
                                                    hipStream_t s) {
+  if (nt == 2) {
+    switch (mtt) {
+      case 1: return launch_a8_g<LOWBIT_BITS, 1, 2>(p, sz, s);
+      case 2: return launch_a8_g<LOWBIT_BITS, 2, 2>(p, sz, s);
+      default: return launch_a8_g<LOWBIT_BITS, 4, 2>(p, sz, s);
+    }
+  }
   switch (mtt) {
-    case 1: return launch_a8_g<LOWBIT_BITS, 1>(p, sz, s);
-    case 2: return launch_a8_g<LOWBIT_BITS, 2>(p, sz, s);
-    default: return launch_a8_g<LOWBIT_BITS, 4>(p, sz, s);
+    case 1: return launch_a8_g<LOWBIT_BITS, 1, 1>(p, sz, s);
+    case 2: return launch_a8_g<LOWBIT_BITS, 2, 1>(p, sz, s);
+    default: return launch_a8_g<LOWBIT_BITS, 4, 1>(p, sz, s);
   }
 }
 

@@ -38,7 +38,7 @@ ABI_VERSION = 3
 # schedule overrides (include/lowbit_tuning.h)
 TUNE_KEYS = {"qmv_block": 0, "qmv_variant": 1, "qmm_blocks": 2, "qmm_mtt": 3, "qmm_kgroups": 4,
              "qmm_nt": 5, "qmm_waves": 6, "qmm_rgroups": 7, "qmm_small_m": 8,
-             "a8_mtt": 9}
+             "a8_mtt": 9, "a8_nt": 10}
 MAX_MULTI = 8   # LOWBIT_MAX_MULTI
 
 

@@ -35,7 +35,9 @@ typedef enum lowbit_tuning_key {
                                    1 = not used)                                    */
   LOWBIT_TUNE_A8_MTT = 9,       /* int8-activation linear: 16-row tiles per block
                                    (1, 2 or 4)                                      */
-  LOWBIT_TUNE_COUNT = 10
+  LOWBIT_TUNE_A8_NT = 10,       /* int8-activation linear: 16-column tiles per wave
+                                   (1 or 2)                                         */
+  LOWBIT_TUNE_COUNT = 11
 } lowbit_tuning_key;
 
 /* Set (value > 0) or clear (value == 0) one override.  LOWBIT_ERR_INVALID_ARG

@@ -178,7 +178,8 @@ def test_quantize_validation(lowbit_lib, args, status):
 
 
 def test_tuning_validation(lowbit_lib):
-    assert lowbit_lib.lowbit_set_tuning(10, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(11, 1) == INVALID
+    assert lowbit_lib.lowbit_set_tuning(10, 2) == OK and lowbit_lib.lowbit_set_tuning(10, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(9, 2) == OK and lowbit_lib.lowbit_set_tuning(9, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(7, 2) == OK and lowbit_lib.lowbit_set_tuning(7, 0) == OK
     assert lowbit_lib.lowbit_set_tuning(-1, 1) == INVALID

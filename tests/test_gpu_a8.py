@@ -98,7 +98,7 @@ def test_act_quant_nonfinite_and_zero_rows(act):
 
 # ---------------------------------------------------------------- linear --
 
-def run_linear_case(M, N, K, bits, group, act, seed, bias=True, mtt=None):
+def run_linear_case(M, N, K, bits, group, act, seed, bias=True, mtt=None, nt=None):
     r, packed, s, z = quant_weights(N, K, bits, group, act, seed)
     x = x_rows(M, K, act, seed + 1)
     xq_ref, a_ref = oracle.quantize_activations_i8(x.float().numpy())
@@ -112,14 +112,14 @@ def run_linear_case(M, N, K, bits, group, act, seed, bias=True, mtt=None):
     xq_d = torch.from_numpy(xq_ref).to(DEV)
     a_d = torch.from_numpy(a_ref).to(DEV)
     b_d = None if b is None else b.to(DEV)
-    with lowbit.tuning(a8_mtt=mtt or 0):
+    with lowbit.tuning(a8_mtt=mtt or 0, a8_nt=nt or 0):
         y = lowbit.lowbit_linear_a8(xq_d, a_d, packed, s, z, b_d, bits, group)
     torch.cuda.synchronize()
     nan_rows = np.isnan(a_ref)
     yc = y.float().cpu()
     assert torch.isnan(yc[torch.from_numpy(nan_rows)]).all()
     keep = ~nan_rows
-    label = f"a8 b{bits} g{group} {act} M={M} N={N} K={K} mtt={mtt}"
+    label = f"a8 b{bits} g{group} {act} M={M} N={N} K={K} mtt={mtt} nt={nt}"
     check_close(y[torch.from_numpy(keep).to(DEV)], y_ref[keep], A[keep], label)
     return y
 
@@ -131,7 +131,8 @@ def test_linear_a8_every_width_and_group(bits, group):
     K = {32: 416, 64: 448, 128: 384, 256: 512}[group]
     act = ["bf16", "f16", "f32"][(bits + group // 32) % 3]
     for mtt in (1, 2, 4):
-        run_linear_case(37, 200, K, bits, group, act, seed=bits * 10 + group, mtt=mtt)
+        for nt in (1, 2):
+            run_linear_case(37, 200, K, bits, group, act, seed=bits * 10 + group, mtt=mtt, nt=nt)
 
 
 @pytest.mark.parametrize("act", ["bf16", "f16", "f32"])
