@@ -515,16 +515,18 @@ constexpr int64_t kA8MaxM = int64_t(1) << 20;
 
 // Tiles of the int8-activation linear: 16-row tiles per block (mtt) and
 // 16-column tiles per wave (nt).  The kernel is bound by its vector-memory
-// instructions; per 16 x 16 output tile and 64-wide K window it issues about
-// 1/nt activation loads, 1/mtt code loads and 1/4 scale/zero loads, so the
-// largest tiles win as long as the launch keeps at least 3.5 waves per CU
-// (measured at M = 128, bits 4, group 32: K = 4096, N = 14336 runs fastest
-// with mtt 4, nt 2 at 3.5 waves per CU, 67 us against 84 us with mtt 2, nt 2
-// at 7; K = 14336, N = 4096 with mtt 2, nt 1 at 4 waves per CU, 92 us,
-// against 132-210 us for larger tiles at 2 waves per CU).
+// instructions.  The block's waves share the activation fragments through
+// LDS, so per 16 x 16 output tile and 64-wide K window a wave issues about
+// 1/(4 nt) activation loads, 1/mtt code loads and 1/4 scale/zero loads: the
+// row tiles matter most, and the largest tiles win as long as the launch
+// keeps at least 3.5 waves per CU (measured at M = 128, bits 4, group 32:
+// K = 4096, N = 14336 runs fastest with mtt 4, nt 1 at 7 waves per CU,
+// 58 us, against 67 us for mtt 4, nt 2 at 3.5; K = 14336, N = 4096 with
+// mtt 2, nt 1 at 4 waves per CU, 82 us, against 134-222 us for larger tiles
+// at 2 waves per CU).
 constexpr int kA8HalfWavesPerCu = 7;
 void a8_tiles(int64_t M, int64_t N, int* mtt_out, int* nt_out) {
-  static const int kOrder[][2] = {{4, 2}, {2, 2}, {4, 1}, {2, 1}, {1, 2}, {1, 1}};
+  static const int kOrder[][2] = {{4, 1}, {2, 1}, {4, 2}, {2, 2}, {1, 1}, {1, 2}};
   const int64_t target = (int64_t(kA8HalfWavesPerCu) * device_cus() + 1) / 2;
   int mtt = 1, nt = 1;
   for (const auto& c : kOrder) {

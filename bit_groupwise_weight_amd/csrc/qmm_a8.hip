@@ -26,16 +26,20 @@
 //
 // Block: 4 waves, each NT 16-column tiles over MTT 16-row tiles and all of
 // K (the activation operand and its row sums X serve the NT column tiles).
-// The operands of 8 / MTT windows are loaded one such batch ahead.  No LDS
-// and no barriers: a wave past N returns at once.
+// The operands of 8 / MTT windows are loaded one such batch ahead; the
+// activation fragments of a batch, the same for every wave of the block,
+// are loaded a quarter per wave and shared through two LDS slabs, one
+// barrier per batch (without a memory fence: the code and scale loads of
+// the next batch stay in flight).  Every wave runs every barrier: a wave
+// past N computes clamped columns and stores nothing.
 //
 // What bounds it: the vector-memory address unit, not the MFMAs (counters at
 // M = 128, K = 4096, N = 14336 with one column tile and one load per scale:
 // the address unit busy 82 % of the kernel and stalled on the cache 55 %,
 // VALU and MFMA mostly idle).  Every load instruction occupies it about the
 // same whatever its width, so the kernel issues few, wide ones: per 16 x 16
-// output tile and window about 1/NT activation loads, 1/MTT code loads and
-// (groups of 32) 1/4 scale/zero loads, the scales and zeros of a batch
+// output tile and window about 1/(4 NT) activation loads, 1/MTT code loads
+// and (groups of 32) 1/4 scale/zero loads, the scales and zeros of a batch
 // coming as one vector per column tile.
 #include "qmm_common.h"
 
@@ -129,8 +133,8 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
   using T = typename Act<SZ>::bits_t;
   constexpr int TB = static_cast<int>(sizeof(T));
   const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 * NT;
-  if (n0 >= p.N) return;
+  const int wv = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * 4 + wv) * 16 * NT;   // waves past N compute clamped columns, store nothing
   const int c = lane & 15;
   const uint32_t j = lane >> 4;
   const int m0 = blockIdx.y * 16 * MTT;
@@ -176,9 +180,30 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
   constexpr int SZW = (SG * TB + 3) / 4;
   struct Batch {
     CodeWords<BITS> cw[U][NT];
-    i32x4_t a[U][MTT];
     uint32_t sw[NT][SZW], zw[NT][SZW];
   };
+  // The activation fragments of a batch, (window, row tile) f = u * MTT + t,
+  // are the same for every wave of the block: each wave loads two of the
+  // eight one batch ahead and writes them to one of two LDS slabs, which all
+  // four waves read.
+  constexpr int NF = U * MTT;   // 8
+  static_assert(NF == 8, "two fragments per wave");
+  __shared__ i32x4_t s_a[2][NF][64];
+  auto load_frags = [&](int bi, i32x4_t (&fr)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int f = 2 * wv + i, u = f / MTT, t = f % MTT;
+      const int w = min(bi * U + u, W - 1);
+      fr[i] = *reinterpret_cast<const i32x4_t*>(arow[t] + lane_k(w));
+    }
+  };
+  auto store_frags = [&](int buf, const i32x4_t (&fr)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s_a[buf][2 * wv + i][lane] = fr[i];
+  };
+  // LDS writes done, then meet the other waves; no memory fence, so the
+  // global loads in flight stay in flight
+  auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
   // Groups of 32: the 2U scales (and zeros) of a batch are contiguous in the
   // row and come in one vector load per column tile when their start is
   // 4-byte aligned and the batch lies inside the row (every load instruction
@@ -238,8 +263,6 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
       const uint32_t kk = lane_k(w);
 #pragma unroll
       for (int q = 0; q < NT; ++q) load_code_words<BITS>(wrow[q], kk, bt.cw[u][q]);
-#pragma unroll
-      for (int t = 0; t < MTT; ++t) bt.a[u][t] = *reinterpret_cast<const i32x4_t*>(arow[t] + kk);
     }
   };
   // value g (0 .. SG-1) of a batch's raw words, as fp32
@@ -286,8 +309,14 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
 
   const int NB = (W + U - 1) / U;
   Batch cur;
+  i32x4_t fr[2];
+  load_frags(0, fr);
   load_batch(0, cur);
+  store_frags(0, fr);
+  lds_barrier();
+  load_frags(min(1, NB - 1), fr);
   for (int bi = 0; bi < NB; ++bi) {
+    const int buf = bi & 1;
     Batch nxt;
     load_batch(min(bi + 1, NB - 1), nxt);   // the last batch loads itself again
 #pragma unroll
@@ -305,18 +334,20 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
           const i32x4_t oh = h == 0 ? ones0 : ones1;
 #pragma unroll
           for (int t = 0; t < MTT; ++t) {
-            X[t] = mfma_i8(cur.a[u][t], oh, zero4);
+            const i32x4_t at = s_a[buf][u * MTT + t][lane];
+            X[t] = mfma_i8(at, oh, zero4);
 #pragma unroll
-            for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(cur.a[u][t], b[q] & keep, zero4);
+            for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(at, b[q] & keep, zero4);
           }
           rescale(cur, 2 * u + h);
         }
       } else {
 #pragma unroll
         for (int t = 0; t < MTT; ++t) {
-          X[t] = mfma_i8(cur.a[u][t], ones, X[t]);
+          const i32x4_t at = s_a[buf][u * MTT + t][lane];
+          X[t] = mfma_i8(at, ones, X[t]);
 #pragma unroll
-          for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(cur.a[u][t], b[q], P[t][q]);
+          for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(at, b[q], P[t][q]);
         }
         if (((w + 1) & ((1 << wg_shift) - 1)) == 0) {   // last window of its group
           rescale(cur, u);
@@ -330,6 +361,11 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
       }
     }
     cur = nxt;
+    // the next batch's fragments into the other slab (last read one batch
+    // ago, before the previous barrier), then the one after that in flight
+    store_frags(buf ^ 1, fr);
+    lds_barrier();
+    load_frags(min(bi + 2, NB - 1), fr);
   }
 
   // D layout of a 16x16 MFMA tile: lane l holds rows 4 (l / 16) + i of column l % 16
