@@ -51,11 +51,13 @@ ROTATE_BYTES = 1 << 30
 # kernel sources whose sha256 prefix is `src_hash`; for any other sources bench
 # reports traffic as null.
 MEASURED_TRAFFIC = {
-    "src_hash": "5f9d6d084eec465f",
-    "qmv_bits1to7_bytes": 67126448,
-    "qmm_bytes": {"4096x14336": 72811725, "14336x4096": 95351268},
+    "src_hash": "0656c1c4fb5ed8c7",
+    "qmv_bits1to7_bytes": 67127087,
+    "qmm_bytes": {"4096x14336": 72811220, "14336x4096": 95352008},
     # rocprofv3 MfmaUtil (%) of the main MFMA kernel per shape
-    "qmm_mfma_util": {"4096x14336": 19.78, "14336x4096": 20.13},
+    "qmm_mfma_util": {"4096x14336": 19.65, "14336x4096": 20.14},
+    # HBM bytes per launch of the int8-activation linear per (K x N) shape
+    "a8_bytes": {"4096x14336": 48982887, "14336x4096": 52535460},
 }
 
 
@@ -745,7 +747,10 @@ def main():
             "unit": "TOP/s",
             "frac": round(sum(2.0 * r["M"] * r["N"] * r["K"] for r in a8)
                           / (sum(r["linear_us"] for r in a8) * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS, 4),
-            "traffic": None,
+            "traffic": (sum(MEASURED_TRAFFIC["a8_bytes"].get(f"{r['K']}x{r['N']}", 0) for r in a8)
+                        if fresh and len(MEASURED_TRAFFIC["a8_bytes"]) == len(a8) else None),
+            "traffic_note": "HBM bytes of one launch of each shape's linear (rocprofv3, scaled); "
+                            "algorithmic bytes: codes + scales + zeros + int8 x + row scales + y",
         },
         "qmv_eager_us_per_call": None if eager_us is None else [round(u, 3) for u in eager_us],
         "qmv_eager_us_per_call_generic": None if eager_generic_us is None
