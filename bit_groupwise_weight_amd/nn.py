@@ -18,7 +18,13 @@ Ops (namespace ``lowbit``):
   ``N x (K/group)`` in ``sz_dtype``;
 * ``lowbit::linear(Tensor x, Tensor packed, Tensor scales, Tensor zeros,
   Tensor? bias, int bits, int group) -> Tensor`` -- ``x[..., K]`` to
-  ``y[..., N]`` in x's dtype, ``y = x . dequant(W)^T (+ bias)``.
+  ``y[..., N]`` in x's dtype, ``y = x . dequant(W)^T (+ bias)``;
+* ``lowbit::linear_a8(...)`` -- the same signature with 8-bit dynamic
+  activations: each row of x is quantized on the fly to int8 codes with one
+  fp32 scale (symmetric, max |x| / 127), and the linear runs over the codes
+  on the int8 matrix cores (the export mode with 8-bit dynamic activations
+  and 4-bit weights in groups of 32 of "[MPS] Add support for Int4 groupwise
+  quantization").
 
 Both run in liblowbit.so through :mod:`bit_groupwise_weight_amd.lowbit`;
 nothing here computes on the CPU.
@@ -108,6 +114,25 @@ def _linear_fake(x, packed, scales, zeros, bias, bits, group):
     return x.new_empty((*x.shape[:-1], N))
 
 
+@torch.library.custom_op("lowbit::linear_a8", mutates_args=())
+def linear_a8(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+              bias: Optional[torch.Tensor], bits: int, group: int) -> torch.Tensor:
+    N, K = _check_linear_shapes(x, packed, scales, zeros, bias, bits, group)
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, K).contiguous()
+    xq, ascale = _lb.lowbit_quantize_act_i8(x2)
+    y = _lb.lowbit_linear_a8(xq, ascale, packed.contiguous(), scales.contiguous(),
+                             zeros.contiguous(), None if bias is None else bias.contiguous(),
+                             bits, group)
+    return y.reshape(*lead, N)
+
+
+@linear_a8.register_fake
+def _linear_a8_fake(x, packed, scales, zeros, bias, bits, group):
+    N, _ = _check_linear_shapes(x, packed, scales, zeros, bias, bits, group)
+    return x.new_empty((*x.shape[:-1], N))
+
+
 # --------------------------------------------------------------- module --
 
 class LowbitLinear(torch.nn.Module):
@@ -116,13 +141,18 @@ class LowbitLinear(torch.nn.Module):
     Buffers: ``packed`` (uint8, ``[N, K*bits/8]``), ``scales`` and ``zeros``
     (``[N, K/group]``, activation dtype) and optional ``bias`` (``[N]``).
     Inputs must be on the GPU, in the activation dtype, with last dim K.
+    ``act_bits=8`` quantizes the activations too, per row to int8 on every
+    call (``lowbit::linear_a8``); ``None`` keeps them floating point.
     """
 
     def __init__(self, in_features: int, out_features: int, bits: int, group_size: int,
                  bias: bool = True, dtype: torch.dtype = torch.float16,
-                 device: Optional[torch.device] = None):
+                 device: Optional[torch.device] = None, act_bits: Optional[int] = None):
         super().__init__()
         _check_bits_group(bits, group_size)
+        if act_bits not in (None, 8):
+            raise ValueError(f"act_bits must be None or 8, got {act_bits}")
+        self.act_bits = act_bits
         if dtype not in _SZ_DTYPES:
             raise ValueError(f"dtype must be one of {_SZ_DTYPES}")
         if in_features % group_size != 0:
@@ -159,14 +189,18 @@ class LowbitLinear(torch.nn.Module):
 
     @classmethod
     def from_linear(cls, lin: torch.nn.Linear, bits: int, group_size: int,
-                    dtype: Optional[torch.dtype] = None) -> "LowbitLinear":
+                    dtype: Optional[torch.dtype] = None,
+                    act_bits: Optional[int] = None) -> "LowbitLinear":
         """Quantize ``lin`` on the fly (its weight must live on the GPU)."""
         dt = dtype or (lin.weight.dtype if lin.weight.dtype in _SZ_DTYPES else torch.float16)
         m = cls(lin.in_features, lin.out_features, bits, group_size, bias=lin.bias is not None,
-                dtype=dt, device=lin.weight.device)
+                dtype=dt, device=lin.weight.device, act_bits=act_bits)
         return m.set_weight(lin.weight, lin.bias)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if self.act_bits == 8:
+            return torch.ops.lowbit.linear_a8(x, self.packed, self.scales, self.zeros, self.bias,
+                                              self.bits, self.group_size)
         # Traced (torch.compile), autograd and non-GPU (e.g. meta) calls go
         # through the registered op; plain eager GPU calls take the prepared
         # call, which validated the weights once (buffers replaced by .to()
@@ -189,26 +223,29 @@ class LowbitLinear(torch.nn.Module):
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, bits={self.bits}, "
-                f"group_size={self.group_size}, dtype={self.dtype}, bias={self.bias is not None}")
+                f"group_size={self.group_size}, dtype={self.dtype}, bias={self.bias is not None}"
+                + ("" if self.act_bits is None else f", act_bits={self.act_bits}"))
 
 
 def quantize_linears(model: torch.nn.Module, bits: int, group_size: int,
                      dtype: Optional[torch.dtype] = None,
-                     filter_fn: Optional[Callable[[torch.nn.Module, str], bool]] = None) -> torch.nn.Module:
+                     filter_fn: Optional[Callable[[torch.nn.Module, str], bool]] = None,
+                     act_bits: Optional[int] = None) -> torch.nn.Module:
     """Replace every ``nn.Linear`` of ``model`` (in place) by a LowbitLinear.
 
     ``filter_fn(module, qualified_name)`` may exclude layers; layers whose
     in_features is not a multiple of ``group_size`` are left as they are.
+    ``act_bits=8`` makes every swapped layer quantize its activations too.
     """
     for name, child in list(model.named_children()):
-        _swap(model, name, child, name, bits, group_size, dtype, filter_fn)
+        _swap(model, name, child, name, bits, group_size, dtype, filter_fn, act_bits)
     return model
 
 
-def _swap(parent, name, child, qual, bits, group_size, dtype, filter_fn):
+def _swap(parent, name, child, qual, bits, group_size, dtype, filter_fn, act_bits):
     if isinstance(child, torch.nn.Linear):
         if child.in_features % group_size == 0 and (filter_fn is None or filter_fn(child, qual)):
-            setattr(parent, name, LowbitLinear.from_linear(child, bits, group_size, dtype))
+            setattr(parent, name, LowbitLinear.from_linear(child, bits, group_size, dtype, act_bits))
         return
     for n, c in list(child.named_children()):
-        _swap(child, n, c, f"{qual}.{n}", bits, group_size, dtype, filter_fn)
+        _swap(child, n, c, f"{qual}.{n}", bits, group_size, dtype, filter_fn, act_bits)

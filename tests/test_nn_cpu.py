@@ -18,6 +18,25 @@ def meta_weights(N, K, bits, group, dtype):
 def test_ops_registered():
     assert hasattr(torch.ops.lowbit, "linear")
     assert hasattr(torch.ops.lowbit, "quantize_pack")
+    assert hasattr(torch.ops.lowbit, "linear_a8")
+
+
+@pytest.mark.parametrize("lead", [(), (5,), (2, 3)])
+def test_linear_a8_shape_function(lead):
+    N, K, bits, group = 40, 256, 4, 32
+    packed, s, z = meta_weights(N, K, bits, group, torch.bfloat16)
+    x = torch.empty((*lead, K), dtype=torch.bfloat16, device=META)
+    y = torch.ops.lowbit.linear_a8(x, packed, s, z, None, bits, group)
+    assert y.shape == (*lead, N) and y.dtype == torch.bfloat16 and y.device == META
+
+
+def test_module_act_bits():
+    m = lnn.LowbitLinear(128, 32, 4, 32, dtype=torch.bfloat16, device=META, act_bits=8)
+    assert "act_bits=8" in repr(m)
+    y = m(torch.empty((3, 128), dtype=torch.bfloat16, device=META))
+    assert y.shape == (3, 32)
+    with pytest.raises(ValueError):
+        lnn.LowbitLinear(128, 32, 4, 32, act_bits=4)
 
 
 @pytest.mark.parametrize("bits", range(1, 8))

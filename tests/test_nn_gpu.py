@@ -122,3 +122,35 @@ def test_module_rebinds_replaced_buffers():
     op = torch.ops.lowbit.linear(x, m.packed, m.scales, m.zeros, m.bias, 4, 64)
     torch.cuda.synchronize()
     assert torch.equal(y1, op) and not torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_module_act_bits_matches_oracle(act):
+    # 8-bit dynamic activations: the oracle's int8 codes of x, then its linear
+    bits, group = 4, 32
+    case, W, b = module_case(bits, group, act, bias=True, seed=7, N=130, K=416)
+    lin = torch.nn.Linear(case.K, case.N, device=DEV, dtype=torch.float32)
+    with torch.no_grad():
+        lin.weight.copy_(W.to(DEV))
+        lin.bias.copy_(b.float().to(DEV))
+    m = lnn.LowbitLinear.from_linear(lin, bits, group, dtype=TORCH_ACT[act], act_bits=8)
+    x = torch.randn((2, 5, case.K), generator=torch.Generator().manual_seed(3)).to(TORCH_ACT[act])
+    y = m(x.to(DEV))
+    assert y.shape == (2, 5, case.N) and y.dtype == TORCH_ACT[act]
+    ref = oracle.quantize(W.numpy(), bits, group, act)
+    xq, a = oracle.quantize_activations_i8(x.reshape(-1, case.K).float().numpy())
+    y_ref, A = oracle.linear_a8(xq, a, ref["q"], ref["s"], ref["z"], group, b.float().numpy())
+    check_close(y.reshape(-1, case.N), y_ref, A, f"LowbitLinear act_bits=8 {act}")
+
+
+def test_act_bits_compile_matches_eager():
+    torch.manual_seed(1)
+    model = torch.nn.Sequential(torch.nn.Linear(256, 512), torch.nn.GELU(), torch.nn.Linear(512, 128))
+    model = model.to(DEV).to(torch.bfloat16)
+    lnn.quantize_linears(model, bits=4, group_size=32, act_bits=8)
+    x = torch.randn((20, 256), device=DEV, dtype=torch.bfloat16)
+    eager = model(x)
+    compiled = torch.compile(model, fullgraph=True, backend="aot_eager")
+    out = compiled(x)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
