@@ -510,8 +510,9 @@ const A8Launcher kA8[8] = {nullptr,
                            lowbit::launch_qmm_a8_b6,
                            lowbit::launch_qmm_a8_b7};
 
-// Largest M of the int8-activation linear: 65535 blocks of 16 rows.
-constexpr int64_t kA8MaxM = int64_t(1) << 20;
+// Largest M of the int8-activation linear: 65535 blocks (the grid's y
+// limit) of 16 rows.
+constexpr int64_t kA8MaxM = int64_t(16) * 65535;
 
 // Tiles of the int8-activation linear: 16-row tiles per block (mtt) and
 // 16-column tiles per wave (nt).  The kernel is bound by its vector-memory
@@ -749,7 +750,8 @@ lowbit_status lowbit_linear_a8(const int8_t* xq, const float* ascale, const uint
   g_last_error.clear();
   lowbit_status st = check_common(bits, group, N, K);
   if (st != LOWBIT_OK) return st;
-  if (M < 0 || M > kA8MaxM) return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld not in 0..2^20", (long long)M);
+  if (M < 0 || M > kA8MaxM)
+    return fail(LOWBIT_ERR_INVALID_ARG, "M=%lld not in 0..%lld", (long long)M, (long long)kA8MaxM);
   if (!valid_dtype(dtype)) return fail(LOWBIT_ERR_UNSUPPORTED, "dtype=%d", (int)dtype);
   if (!packed || !scales || !zeros) return fail(LOWBIT_ERR_INVALID_ARG, "NULL weight pointer");
   if (M == 0) return LOWBIT_OK;

@@ -8,7 +8,9 @@
 //   X = sum over group g of xq       (exact in int32)
 //
 // Both integer sums come from v_mfma_i32_16x16x64_i8: P with the codes as
-// the B operand, X with a ones operand, so X lands in the same lanes as P.
+// the B operand, X with a ones operand, so X lands in the same lanes as P
+// (with groups of 32, X is computed once per activation fragment by the wave
+// that loads it and shared as fp32 through LDS).
 // Each group's sums are turned into fp32 and scaled once (two fused
 // multiply-adds per output and group), and a_m and the bias enter once at
 // the store, rounded once to the output type.
@@ -171,6 +173,11 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
     return G32 ? min(2 * w + h, p.groups - 1) : (w >> wg_shift);
   };
 
+  // group-32 passes: the lane groups of pass h are 2h and 2h + 1
+  const i32x4_t keep0 = (j >> 1) == 0 ? i32x4_t{-1, -1, -1, -1} : zero4;
+  const i32x4_t keep1 = (j >> 1) == 1 ? i32x4_t{-1, -1, -1, -1} : zero4;
+  const i32x4_t ones0 = ones & keep0, ones1 = ones & keep1;
+
   // Operands of U consecutive windows (U = 8 / MTT: the activations of a
   // batch take 64 registers at every MTT), loaded one batch ahead.  The
   // scales and zeros of a batch are kept as raw words, SG values of T per
@@ -197,9 +204,25 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
       fr[i] = *reinterpret_cast<const i32x4_t*>(arow[t] + lane_k(w));
     }
   };
+  // Groups of 32: the row sums X of a fragment's two groups (the same for
+  // every column) are computed once, by the wave that loads the fragment,
+  // and shared as fp32 through LDS: s_x[buf][f][h][j] holds rows 4j .. 4j+3.
+  __shared__ float4_t s_x[2][G32 ? NF : 1][2][4];
   auto store_frags = [&](int buf, const i32x4_t (&fr)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) s_a[buf][2 * wv + i][lane] = fr[i];
+    if constexpr (G32) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const i32x4_t x = mfma_i8(fr[i], h == 0 ? ones0 : ones1, zero4);
+          if (c == 0)
+            s_x[buf][2 * wv + i][h][j] = float4_t{static_cast<float>(x[0]), static_cast<float>(x[1]),
+                                                  static_cast<float>(x[2]), static_cast<float>(x[3])};
+        }
+      }
+    }
   };
   // LDS writes done, then meet the other waves; no memory fence, so the
   // global loads in flight stay in flight
@@ -271,10 +294,6 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
     else return act_bits_to_float<SZ>((wd[g >> 1] >> (16 * (g & 1))) & 0xffffu);
   };
 
-  // group-32 passes: the lane groups of pass h are 2h and 2h + 1
-  const i32x4_t keep0 = (j >> 1) == 0 ? i32x4_t{-1, -1, -1, -1} : zero4;
-  const i32x4_t keep1 = (j >> 1) == 1 ? i32x4_t{-1, -1, -1, -1} : zero4;
-  const i32x4_t ones0 = ones & keep0, ones1 = ones & keep1;
 
   float acc[MTT][NT][4];
   i32x4_t P[MTT][NT], X[MTT];
@@ -288,13 +307,19 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
       for (int i = 0; i < 4; ++i) acc[t][q][i] = 0.0f;
     }
   }
-  // acc += s * P + z * X for every tile (X converted once per row tile)
-  auto rescale = [&](const Batch& bt, int g) {
+  // acc += s * P + z * X for every tile (X as fp32: from LDS with groups of
+  // 32, else converted here once per row tile)
+  auto rescale = [&](const Batch& bt, int g, int buf, int u, int h) {
 #pragma unroll
     for (int t = 0; t < MTT; ++t) {
       float xf[4];
+      if constexpr (G32) {
+        const float4_t xv = s_x[buf][u * MTT + t][h][j];
+        xf[0] = xv[0]; xf[1] = xv[1]; xf[2] = xv[2]; xf[3] = xv[3];
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xf[i] = static_cast<float>(X[t][i]);
+        for (int i = 0; i < 4; ++i) xf[i] = static_cast<float>(X[t][i]);
+      }
 #pragma unroll
       for (int q = 0; q < NT; ++q) {
         const float sv = sz_value(bt.sw[q], g), zv = sz_value(bt.zw[q], g);
@@ -331,15 +356,13 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
         for (int h = 0; h < 2; ++h) {
           if (h == 1 && 64u * static_cast<uint32_t>(w) + 64u > K) break;   // a half window
           const i32x4_t keep = h == 0 ? keep0 : keep1;
-          const i32x4_t oh = h == 0 ? ones0 : ones1;
 #pragma unroll
           for (int t = 0; t < MTT; ++t) {
             const i32x4_t at = s_a[buf][u * MTT + t][lane];
-            X[t] = mfma_i8(at, oh, zero4);
 #pragma unroll
             for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(at, b[q] & keep, zero4);
           }
-          rescale(cur, 2 * u + h);
+          rescale(cur, 2 * u + h, buf, u, h);
         }
       } else {
 #pragma unroll
@@ -350,7 +373,7 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
           for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(at, b[q], P[t][q]);
         }
         if (((w + 1) & ((1 << wg_shift) - 1)) == 0) {   // last window of its group
-          rescale(cur, u);
+          rescale(cur, u, buf, u, 0);
 #pragma unroll
           for (int t = 0; t < MTT; ++t) {
             X[t] = zero4;

@@ -267,7 +267,7 @@ lowbit_status lowbit_quantize_act_i8(const void* x, lowbit_dtype act_dtype, int6
  *   y        device, M x N row-major, dtype.  Overwritten; must not alias an
  *            input.
  *   dtype    storage type of scales, zeros, bias and y (fp32, fp16, bf16).
- *   M >= 0 (0 is a no-op), N > 0, K % group == 0, M <= 2^20.
+ *   M >= 0 (0 is a no-op), N > 0, K % group == 0, M <= 16 * 65535.
  *
  * No workspace, one launch, asynchronous.  Deterministic: no atomics, and
  * every output is summed in one fixed order. */

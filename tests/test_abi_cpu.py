@@ -108,7 +108,7 @@ def lin_a8(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=0), INVALID), (dict(bits=8), INVALID), (dict(group=16), INVALID),
     (dict(K=96, group=64), INVALID), (dict(N=0), INVALID), (dict(M=-1), INVALID),
-    (dict(M=(1 << 20) + 1), INVALID), (dict(xq=None), INVALID), (dict(ascale=None), INVALID),
+    (dict(M=16 * 65535 + 1), INVALID), (dict(xq=None), INVALID), (dict(ascale=None), INVALID),
     (dict(y=None), INVALID), (dict(packed=None), INVALID), (dict(zeros=None), INVALID),
     (dict(dt=5), UNSUPPORTED), (dict(xq=A + 4), MISALIGNED), (dict(packed=A + 4), MISALIGNED),
     (dict(ascale=A + 2), MISALIGNED), (dict(y=A + 1), MISALIGNED), (dict(bias=A + 1), MISALIGNED),
