@@ -178,10 +178,10 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
   const i32x4_t keep1 = (j >> 1) == 1 ? i32x4_t{-1, -1, -1, -1} : zero4;
   const i32x4_t ones0 = ones & keep0, ones1 = ones & keep1;
 
-  // Operands of U consecutive windows (U = 8 / MTT: the activations of a
-  // batch take 64 registers at every MTT), loaded one batch ahead.  The
-  // scales and zeros of a batch are kept as raw words, SG values of T per
-  // column tile (two per window with groups of 32, else one).
+  // Operands of U consecutive windows (U = 8 / MTT: a batch holds eight
+  // activation fragments at every MTT, two per wave), loaded one batch
+  // ahead.  The scales and zeros of a batch are kept as raw words, SG values
+  // of T per column tile (two per window with groups of 32, else one).
   constexpr int U = 8 / MTT;
   constexpr int SG = G32 ? 2 * U : U;
   constexpr int SZW = (SG * TB + 3) / 4;
