@@ -167,11 +167,6 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
     const uint32_t kk = 64u * static_cast<uint32_t>(w) + 16u * j;
     return kk >= K ? kk - 32u : kk;
   };
-  // scale/zero index of pass h of window w (G32: group 2w + h, clamped for a
-  // half window; otherwise the window's group)
-  auto sz_index = [&](int w, int h) -> int {
-    return G32 ? min(2 * w + h, p.groups - 1) : (w >> wg_shift);
-  };
 
   // group-32 passes: the lane groups of pass h are 2h and 2h + 1
   const i32x4_t keep0 = (j >> 1) == 0 ? i32x4_t{-1, -1, -1, -1} : zero4;
@@ -227,13 +222,19 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
   // LDS writes done, then meet the other waves; no memory fence, so the
   // global loads in flight stay in flight
   auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
-  // Groups of 32: the 2U scales (and zeros) of a batch are contiguous in the
-  // row and come in one vector load per column tile when their start is
-  // 4-byte aligned and the batch lies inside the row (every load instruction
-  // costs the address unit about the same, whatever its width); otherwise
-  // one load per group.
-  const bool sz_wide = G32 && (TB == 4 || (p.groups % 2 == 0)) &&
+  // The scales (and zeros) of a batch are SG consecutive groups of the row,
+  // slot i holding group g0 + i (g0: the batch's first group, rounded down
+  // to an even group for 2-byte values so that the slots start 4-byte
+  // aligned); they come in one vector load per column tile when the slots
+  // lie inside the row and the rows are 4-byte aligned (every load
+  // instruction costs the address unit about the same, whatever its width),
+  // otherwise one load per group.
+  const bool sz_wide = (TB == 4 || (p.groups % 2 == 0)) &&
                        ((reinterpret_cast<uintptr_t>(p.scales) | reinterpret_cast<uintptr_t>(p.zeros)) & 3u) == 0;
+  auto batch_g0 = [&](int bi) -> int {
+    if constexpr (G32) return SG * bi;
+    else return TB == 2 ? ((bi * U) >> wg_shift) & ~1 : ((bi * U) >> wg_shift);
+  };
   auto load_words = [&](const T* src, uint32_t (&wd)[SZW]) {
     const uint32_t* s4 = static_cast<const uint32_t*>(__builtin_assume_aligned(src, 4));
     if constexpr (SZW % 4 == 0) {
@@ -250,19 +251,15 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
     }
   };
   auto load_batch = [&](int bi, Batch& bt) {
-    bool wide = false;
-    if constexpr (G32) {
-      const int g0 = SG * bi;
-      if (sz_wide && g0 + SG <= p.groups) {
-        wide = true;
+    const int g0 = batch_g0(bi);
+    const bool wide = sz_wide && g0 + SG <= p.groups;
+    if (wide) {
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          load_words(srow[q] + g0, bt.sw[q]);
-          load_words(zrow[q] + g0, bt.zw[q]);
-        }
+      for (int q = 0; q < NT; ++q) {
+        load_words(srow[q] + g0, bt.sw[q]);
+        load_words(zrow[q] + g0, bt.zw[q]);
       }
-    }
-    if (!wide) {
+    } else {
 #pragma unroll
       for (int q = 0; q < NT; ++q) {
 #pragma unroll
@@ -272,8 +269,7 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
         }
 #pragma unroll
         for (int g = 0; g < SG; ++g) {
-          const int w = min(bi * U + (G32 ? g / 2 : g), W - 1);
-          const int idx = sz_index(w, G32 ? g % 2 : 0);
+          const int idx = min(g0 + g, p.groups - 1);
           const uint32_t sh = 8u * static_cast<uint32_t>((g * TB) % 4);
           bt.sw[q][(g * TB) / 4] |= static_cast<uint32_t>(srow[q][idx]) << sh;
           bt.zw[q][(g * TB) / 4] |= static_cast<uint32_t>(zrow[q][idx]) << sh;
@@ -288,10 +284,29 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
       for (int q = 0; q < NT; ++q) load_code_words<BITS>(wrow[q], kk, bt.cw[u][q]);
     }
   };
-  // value g (0 .. SG-1) of a batch's raw words, as fp32
+  // slot g (0 .. SG-1) of a batch's raw words, as fp32: g a compile-time
+  // constant (groups of 32), or (groups of 64 and more) a wave-uniform index
+  // known only at run time, picked by selects over the slots (an array
+  // indexed at run time would live in scratch)
+  auto sz_slot = [&](const uint32_t (&wd)[SZW], int i) -> float {
+    if constexpr (TB == 4) return __uint_as_float(wd[i]);
+    else return act_bits_to_float<SZ>((wd[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+  };
   auto sz_value = [&](const uint32_t (&wd)[SZW], int g) -> float {
-    if constexpr (TB == 4) return __uint_as_float(wd[g]);
-    else return act_bits_to_float<SZ>((wd[g >> 1] >> (16 * (g & 1))) & 0xffffu);
+    if constexpr (G32) {
+      return sz_slot(wd, g);
+    } else {
+      // (each slot made opaque first: a select chain over plain array
+      // elements would be folded back into an indexed access)
+      float v = sz_slot(wd, 0);
+#pragma unroll
+      for (int i = 1; i < SG; ++i) {
+        float t = sz_slot(wd, i);
+        asm("" : "+v"(t));
+        v = g == i ? t : v;
+      }
+      return v;
+    }
   };
 
 
@@ -373,7 +388,7 @@ __global__ __launch_bounds__(256) void qmm_a8_kernel(A8Params p) {
           for (int q = 0; q < NT; ++q) P[t][q] = mfma_i8(at, b[q], P[t][q]);
         }
         if (((w + 1) & ((1 << wg_shift) - 1)) == 0) {   // last window of its group
-          rescale(cur, u, buf, u, 0);
+          rescale(cur, (w >> wg_shift) - batch_g0(bi), buf, u, 0);
 #pragma unroll
           for (int t = 0; t < MTT; ++t) {
             X[t] = zero4;
