@@ -141,6 +141,16 @@ def test_linear_a8_dtypes(act, bits, group):
     run_linear_case(20, 96, 2048 + 32 * (group == 32), bits, group, act, seed=3, bias=act != "f32")
 
 
+@pytest.mark.parametrize("group", [64, 128, 256])
+@pytest.mark.parametrize("act", ["bf16", "f16", "f32"])
+def test_linear_a8_batched_scales(group, act):
+    # an even number of groups and many batches: the scales and zeros of a
+    # batch come in one load, from an even start slot for 2-byte values
+    for mtt in (1, 2, 4):
+        for nt in (1, 2):
+            run_linear_case(37, 150, 3072, 4, group, act, seed=group + mtt, mtt=mtt, nt=nt)
+
+
 @pytest.mark.parametrize("M", [1, 2, 16, 17, 64, 129])
 def test_linear_a8_row_counts(M):
     run_linear_case(M, 130, 1024, 4, 32, "bf16", seed=M)
